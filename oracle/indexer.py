@@ -1,0 +1,162 @@
+"""CPU oracle of the DSA indexer decode step -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import or call this module. The product path (the HIP
+library and its Python binding) never does, and this module imports nothing
+from the product path: the two share no code. It is plain numpy in float64,
+deliberately slow and direct so that it can be checked against the pages by
+eye.
+
+What it computes, and where the pages state it:
+
+* Paged key walk (page "The Moment of Breakthrough", section "The Context";
+  page "The O(Actual) Indexer", section "The Bottleneck That Was"): keys are
+  c4-compressed, 64 positions per page, and the widest row is
+  ``page_table.shape[1] * 64`` positions. Position s of request b reads page
+  ``page_table[b, s // 64]`` at row ``s % 64``.
+* Score (page "The O(Actual) Indexer", section "The Bottleneck That Was": the
+  fallback's batched product of 32 heads of 64-dim queries against every
+  position, followed by clamp_min, mul and sum over heads): for each valid
+  position, ``score = sum_h w[b,h] * max(0, q[b,h,:] . k[s,:])``.
+* Mask (same section, and section "The Benchmark Results" on the full-size
+  output the downstream top-k needs): every position at or past the request's
+  length is -inf, and the output always has the full row width.
+* Top-k (section "The Benchmark Results": the downstream top-k over the
+  logits): the k largest scores of positions [0, L) per request.
+
+Readings taken where the pages are silent (each is listed in the design
+notes): lengths are clamped to [0, row width]; a page id outside the pool in a
+slot that holds valid positions gives NaN for that page's valid positions;
+slots past the last valid page are never read; top-k orders by score
+descending with the lower index first among equal scores, treats -0 and +0 as
+equal and NaN as below every number, returns min(k, L) indices in ascending
+index order and pads the rest with -1.
+
+Every function here is pinned by CPU tests against brute force, closed forms
+and invariants; none is pinned by the HIP path.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+PAGE = 64  # c4 positions per page (a 256-token page, 4 tokens per c4 key)
+
+
+def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
+    """bfloat16 bit patterns -> float64 (exact: bf16 is the top half of f32)."""
+    u32 = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
+    return u32.view(np.float32).astype(np.float64)
+
+
+def clamp_len(length: int, row_width: int) -> int:
+    return int(min(max(int(length), 0), row_width))
+
+
+def gather_keys(k_bits: np.ndarray, table_row: np.ndarray, length: int):
+    """Keys of positions [0, length) of one request, as float64 [length, D],
+    and a boolean [length] flag of positions whose page id is outside the pool."""
+    num_pages = k_bits.shape[0]
+    n_slots = (length + PAGE - 1) // PAGE
+    pages = np.asarray(table_row[:n_slots], dtype=np.int64)
+    bad_page = (pages < 0) | (pages >= num_pages)
+    safe = np.where(bad_page, 0, pages)
+    keys = bf16_bits_to_f64(k_bits[safe]).reshape(n_slots * PAGE, -1)[:length]
+    bad = np.repeat(bad_page, PAGE)[:length]
+    return keys, bad
+
+
+def score(q_bits, w, k_bits, page_table, seq_lens) -> np.ndarray:
+    """Logits [B, max_pages * 64] in float64: scores below each request's
+    length, -inf at and past it (NaN where the page id is outside the pool).
+
+    q_bits uint16 [B, H, D]; w float32 [B, H]; k_bits uint16 [P, 64, D];
+    page_table int32 [B, max_pages]; seq_lens int32 [B].
+    """
+    q = bf16_bits_to_f64(q_bits)
+    w64 = np.asarray(w, dtype=np.float64)
+    B = q.shape[0]
+    N = page_table.shape[1] * PAGE
+    out = np.full((B, N), -np.inf, dtype=np.float64)
+    for b in range(B):
+        L = clamp_len(seq_lens[b], N)
+        if L == 0:
+            continue
+        keys, bad = gather_keys(k_bits, page_table[b], L)
+        dots = q[b] @ keys.T  # [H, L]: every head's dot product with every key
+        relu = np.maximum(dots, 0.0)
+        row = w64[b] @ relu  # sum over heads of w_h * ReLU(dot_h)
+        row[bad] = np.nan
+        out[b, :L] = row
+    return out
+
+
+def score_at(q_bits, w, k_bits, page_table, seq_lens, b: int, s: int) -> float:
+    """One logit, computed on its own (for sampled checks at full size)."""
+    N = page_table.shape[1] * PAGE
+    L = clamp_len(seq_lens[b], N)
+    if s >= L:
+        return float("-inf")
+    p = int(page_table[b, s // PAGE])
+    if p < 0 or p >= k_bits.shape[0]:
+        return float("nan")
+    key = bf16_bits_to_f64(k_bits[p, s % PAGE])
+    q = bf16_bits_to_f64(q_bits[b])
+    dots = q @ key
+    return float(np.dot(np.asarray(w[b], dtype=np.float64), np.maximum(dots, 0.0)))
+
+
+def score_magnitudes(q_bits, w, k_bits, page_table, seq_lens):
+    """Per-position sizes that bound the rounding error of any evaluation of
+    the score in lower precision (for tolerances; same layout as ``score``).
+
+    M[b,s] = sum_h |w_h| * |q_h . k_s|            (size of the head terms)
+    A[b,s] = sum_h |w_h| * sum_d |q_hd * k_sd|    (size of the products)
+    Both are 0 at masked positions.
+    """
+    q = bf16_bits_to_f64(q_bits)
+    w64 = np.abs(np.asarray(w, dtype=np.float64))
+    B = q.shape[0]
+    N = page_table.shape[1] * PAGE
+    M = np.zeros((B, N))
+    A = np.zeros((B, N))
+    for b in range(B):
+        L = clamp_len(seq_lens[b], N)
+        if L == 0:
+            continue
+        keys, _ = gather_keys(k_bits, page_table[b], L)
+        M[b, :L] = w64[b] @ np.abs(q[b] @ keys.T)
+        A[b, :L] = w64[b] @ (np.abs(q[b]) @ np.abs(keys).T)
+    return M, A
+
+
+def topk(logits: np.ndarray, seq_lens, k: int) -> np.ndarray:
+    """Top-k positions per request as int64 [B, k].
+
+    Ranks positions [0, L) by score descending, lower index first on equal
+    scores (-0 == +0), NaN last; keeps the first min(k, L); returns them in
+    ascending index order followed by -1 padding.
+    """
+    logits = np.asarray(logits)
+    B, N = logits.shape
+    out = np.full((B, k), -1, dtype=np.int64)
+    for b in range(B):
+        L = clamp_len(seq_lens[b], N)
+        x = logits[b, :L].astype(np.float64)
+        idx = np.arange(L)
+        nan = np.isnan(x)
+        neg = np.where(nan, 0.0, -x)
+        # lexsort: last key is primary -> non-NaN first, then score desc, then index asc
+        order = np.lexsort((idx, neg, nan))
+        chosen = np.sort(order[:min(k, L)])
+        out[b, :chosen.size] = chosen
+    return out
+
+
+def topk_values(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
+    """Scores at the chosen positions (NaN where the slot is padding)."""
+    B, k = idx.shape
+    vals = np.full((B, k), np.nan, dtype=np.asarray(logits).dtype)
+    for b in range(B):
+        sel = idx[b] >= 0
+        vals[b, sel] = logits[b, idx[b, sel]]
+    return vals

@@ -1,0 +1,192 @@
+"""Seeded synthetic inputs for the DSA indexer decode step.
+
+This module only draws random numbers and lays them out; it performs none of
+the indexer's arithmetic. Both the HIP path (through the binding) and the CPU
+oracle consume what it returns, so it imports neither of them.
+
+Geometry (page "The O(Actual) Indexer", section "The Bottleneck That Was";
+page "The Moment of Breakthrough", section "The Context"): keys are kept in
+c4-compressed form, one key per 4 tokens, in pages of 64 c4 positions
+(256 tokens / 4). A request's logical c4 position s lives in page slot s // 64
+of its page-table row, at offset s % 64 inside that physical page, and the
+widest row of logits is ``max_pages * 64`` positions.
+
+Value recipe (same for every config): q and k are standard normal draws in
+float32 rounded to bfloat16 with round-to-nearest-even; w is float32, either
+N(0, 1/32) or |N(0, 1)| / sqrt(32). Lengths are drawn directly in c4 positions,
+uniform over the integer range, which equals a uniform token length that is a
+multiple of 4. Draw order from ``numpy.random.Generator(PCG64(seed))``:
+lengths, page permutation, q, w, k.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+HEADS = 32  # indexer heads
+DIM = 64  # indexer head dimension
+PAGE = 64  # c4 positions per page (256 tokens / 4)
+POISON = -1  # page-table value in slots no valid position maps to
+
+
+@dataclasses.dataclass(frozen=True)
+class Config:
+    name: str
+    batch: int
+    max_pages: int  # page slots per request; max_c4 = max_pages * PAGE
+    len_lo: int  # c4 positions, inclusive
+    len_hi: int  # c4 positions, inclusive
+    topk: int
+    w_kind: str  # "signed": N(0, 1/32); "abs": |N(0,1)| / sqrt(32)
+    pool: str  # "shared": pool = total valid pages; "perm64": tiny's 64-page pool
+    seed: int
+    description: str = ""
+
+    @property
+    def max_c4(self) -> int:
+        return self.max_pages * PAGE
+
+
+CONFIGS = {
+    c.name: c
+    for c in [
+        Config("tiny", 1, 32, 128, 128, 64, "abs", "perm64", 0,
+               "B=1, 8K-token max context (2048 c4), seq_len 512 tokens (128 c4), top-k 64"),
+        Config("c2", 16, 32, 64, 2048, 512, "signed", "shared", 1,
+               "B=16, 8K-token max context, seq_lens uniform in [256, 8192] tokens, top-k 512"),
+        Config("c3", 64, 512, 128, 32768, 2048, "signed", "shared", 2,
+               "B=64, 128K-token max context, seq_lens uniform in [512, 131072] tokens, top-k 2048"),
+        Config("stress1m", 64, 4096, 128, 128, 64, "signed", "shared", 3,
+               "B=64, ~1M-token max context (262144 c4), every seq_len 512 tokens, top-k 64"),
+        Config("stress8k", 64, 32, 128, 128, 64, "signed", "shared", 3,
+               "B=64, 8K-token max context (2048 c4), every seq_len 512 tokens, top-k 64"),
+        Config("full", 64, 512, 32768, 32768, 2048, "signed", "shared", 4,
+               "B=64, 128K-token max context, every seq_len 131072 tokens (all 512 pages valid), top-k 2048"),
+    ]
+}
+
+
+@dataclasses.dataclass
+class Inputs:
+    """Host buffers of one decode step, in the layout the library takes.
+
+    q_bits   uint16 [B, HEADS, DIM]        bfloat16 bit patterns
+    w        float32 [B, HEADS]
+    k_bits   uint16 [num_pages, PAGE, DIM] bfloat16 bit patterns, dim fastest
+    page_table int32 [B, max_pages]        physical page per slot, POISON where unused
+    seq_lens int32 [B]                     valid c4 positions per request
+    """
+
+    q_bits: np.ndarray
+    w: np.ndarray
+    k_bits: np.ndarray
+    page_table: np.ndarray
+    seq_lens: np.ndarray
+    topk: int
+
+    @property
+    def batch(self) -> int:
+        return int(self.q_bits.shape[0])
+
+    @property
+    def max_pages(self) -> int:
+        return int(self.page_table.shape[1])
+
+    @property
+    def max_c4(self) -> int:
+        return self.max_pages * PAGE
+
+    @property
+    def num_pages(self) -> int:
+        return int(self.k_bits.shape[0])
+
+
+def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns, round to nearest, ties to even.
+
+    Inputs here are finite draws, so no NaN handling is needed.
+    """
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+def pages_needed(seq_lens: np.ndarray) -> np.ndarray:
+    """Page slots a request of the given c4 length occupies."""
+    return (np.asarray(seq_lens, dtype=np.int64) + PAGE - 1) // PAGE
+
+
+def _normal_bf16(rng: np.random.Generator, shape) -> np.ndarray:
+    n = int(np.prod(shape))
+    return round_to_bf16_bits(rng.standard_normal(n, dtype=np.float32)).reshape(shape)
+
+
+def generate(cfg: Config | str, seed: int | None = None) -> Inputs:
+    """Draw one decode step's inputs for ``cfg`` (deterministic in the seed)."""
+    if isinstance(cfg, str):
+        cfg = CONFIGS[cfg]
+    rng = np.random.Generator(np.random.PCG64(cfg.seed if seed is None else seed))
+    B, S = cfg.batch, cfg.max_pages
+
+    # 1. lengths
+    if cfg.len_lo == cfg.len_hi:
+        lens = np.full(B, cfg.len_lo, dtype=np.int32)
+    else:
+        lens = rng.integers(cfg.len_lo, cfg.len_hi, size=B, endpoint=True).astype(np.int32)
+    need = pages_needed(lens)
+
+    # 2. page permutation -> page table
+    table = np.full((B, S), POISON, dtype=np.int32)
+    if cfg.pool == "perm64":
+        num_pages = 64
+        perm = rng.permutation(num_pages).astype(np.int32)
+        table[:, :] = perm[:S]
+    else:
+        num_pages = int(need.sum())
+        perm = rng.permutation(num_pages).astype(np.int32)
+        off = 0
+        for b in range(B):
+            n = int(need[b])
+            table[b, :n] = perm[off:off + n]
+            off += n
+
+    # 3. q, 4. w, 5. k
+    q = _normal_bf16(rng, (B, HEADS, DIM))
+    if cfg.w_kind == "abs":
+        w = (np.abs(rng.standard_normal(B * HEADS, dtype=np.float32))
+             / np.float32(math.sqrt(HEADS))).reshape(B, HEADS)
+    else:
+        w = (rng.standard_normal(B * HEADS, dtype=np.float32)
+             * np.float32(1.0 / math.sqrt(HEADS))).reshape(B, HEADS)
+    k = _normal_bf16(rng, (num_pages, PAGE, DIM))
+    return Inputs(q, w.astype(np.float32), k, table, lens, cfg.topk)
+
+
+def random_case(seed: int, batch: int, max_pages: int, lens=None, topk: int = 16,
+                signed_w: bool = True, pool_extra: int = 3, poison: int = POISON) -> Inputs:
+    """A small randomized case for parity sweeps: arbitrary lengths (may be 0,
+    a partial page, or exactly the row width), a pool with spare pages, and
+    unused slots filled with ``poison``."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    N = max_pages * PAGE
+    if lens is None:
+        lens = rng.integers(0, N, size=batch, endpoint=True)
+    lens = np.asarray(lens, dtype=np.int32)
+    need = pages_needed(np.clip(lens, 0, N))
+    num_pages = int(need.sum()) + pool_extra
+    perm = rng.permutation(num_pages).astype(np.int32)
+    table = np.full((batch, max_pages), poison, dtype=np.int32)
+    off = 0
+    for b in range(batch):
+        n = int(need[b])
+        table[b, :n] = perm[off:off + n]
+        off += n
+    q = _normal_bf16(rng, (batch, HEADS, DIM))
+    w = rng.standard_normal(batch * HEADS, dtype=np.float32).reshape(batch, HEADS)
+    w = w * np.float32(1.0 / math.sqrt(HEADS))
+    if not signed_w:
+        w = np.abs(w)
+    k = _normal_bf16(rng, (num_pages, PAGE, DIM))
+    return Inputs(q, w.astype(np.float32), k, table, lens, topk)
