@@ -1,0 +1,141 @@
+/*
+ * dsa_indexer.h -- C ABI of the DSA indexer decode step on MI355X (gfx950).
+ *
+ * One decode step of the DeepSeek sparse-attention (DSA) indexer, as described
+ * on the pages "The O(Actual) Indexer: Validating 128K Context at 500 tok/s on
+ * Blackwell" (sections "The Bottleneck That Was" and "The Benchmark Results")
+ * and "The Moment of Breakthrough: Validating the Indexer Fix" (section "The
+ * Context: A Long Hunt for the Hidden Wall"):
+ *
+ *   1. walk each request's page table over c4-compressed key pages of 64
+ *      positions (a 256-token page, one key per 4 tokens);
+ *   2. score every valid position s of request b as
+ *        score[b][s] = sum_{h<32} w[b][h] * max(0, sum_{d<64} q[b][h][d] * k[s][d])
+ *      with bfloat16 q and k, float32 w and float32 accumulation;
+ *   3. write -inf at every position at or past the request's length, into a
+ *      full-width output of max_pages * 64 positions, skipping the key reads
+ *      and the products for pages past the length (so that the work follows
+ *      the actual length, not the configured maximum);
+ *   4. select the top-k positions of each request.
+ *
+ * Conventions shared by every entry point
+ *   - All buffer pointers are DEVICE pointers owned by the caller. The library
+ *     never allocates, frees, synchronizes, or reads device memory on the host;
+ *     a call validates its scalar arguments and pointers on the host, enqueues
+ *     kernels on `stream` (NULL = the null stream) and returns. Every call can
+ *     be captured into a hipGraph (launch shapes depend only on the scalar
+ *     arguments, never on device data).
+ *   - Errors detectable on the host return a negative dsa_status_t and enqueue
+ *     nothing. A failed launch returns DSA_ERR_HIP; the HIP error code is then
+ *     available from dsa_indexer_last_hip_error() on the same thread.
+ *   - Conditions only the device can see are not errors (reporting them would
+ *     need a synchronization) and are defined instead:
+ *       * seq_lens[b] is clamped to [0, max_pages * 64];
+ *       * a page id outside [0, num_pages) in a slot that holds valid
+ *         positions is never dereferenced; those valid positions score NaN;
+ *       * slots at or past ceil(seq_lens[b] / 64) are never read, so they may
+ *         hold anything (e.g. -1);
+ *       * non-finite q, k or w give unspecified scores.
+ *   - Shapes are fixed by the method: 32 heads, head dim 64, 64 positions per
+ *     page. All arrays are dense, row-major, innermost index last.
+ */
+#ifndef DSA_INDEXER_H
+#define DSA_INDEXER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DSA_INDEXER_ABI_VERSION 1
+#define DSA_INDEXER_HEADS 32 /* indexer heads */
+#define DSA_INDEXER_DIM 64   /* head dimension */
+#define DSA_INDEXER_PAGE 64  /* c4 positions per page */
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = -1,      /* a required pointer is NULL */
+  DSA_ERR_SHAPE = -2,     /* batch, max_pages, num_pages or max_c4 out of range */
+  DSA_ERR_ALIGN = -3,     /* a pointer misses its required alignment */
+  DSA_ERR_K = -4,         /* k out of [1, max_c4] */
+  DSA_ERR_WORKSPACE = -5, /* workspace too small for the call */
+  DSA_ERR_HIP = -6        /* the HIP runtime reported an error for a launch */
+} dsa_status_t;
+
+/* DSA_INDEXER_ABI_VERSION of the loaded library. */
+int dsa_indexer_abi_version(void);
+
+/* Static text for a dsa_status_t value ("unknown status" otherwise). */
+const char *dsa_indexer_status_string(int status);
+
+/* hipError_t of the last DSA_ERR_HIP on the calling thread (0 if none). */
+int dsa_indexer_last_hip_error(void);
+
+/*
+ * Score step (steps 1-3 above): fills logits[b][0 : max_pages*64] for every
+ * request.
+ *
+ *   q          bf16  [batch][32][64], 16-byte aligned
+ *   w          fp32  [batch][32]
+ *   k_pool     bf16  [num_pages][64][64], 16-byte aligned: page p, row i is the
+ *              key of the position that maps to (p, i); dims contiguous
+ *   num_pages  pages in k_pool (> 0)
+ *   page_table int32 [batch][max_pages]: physical page of each slot; position
+ *              s of request b lives in page page_table[b][s / 64], row s % 64
+ *   seq_lens   int32 [batch]: valid c4 positions per request
+ *   batch      1 .. 65535
+ *   max_pages  1 .. 2^22 (row width max_pages * 64 at most 2^28 positions)
+ *   logits     fp32  [batch][max_pages*64], 16-byte aligned; on return of the
+ *              enqueued work: the score for s < seq_lens[b], -inf otherwise
+ *              (bit pattern 0xFF800000)
+ *   row_hwm    NULL, or int32 [batch] high-water marks for the incremental
+ *              tail. With NULL every call writes the whole -inf tail. With a
+ *              buffer, the caller keeps `logits` and `row_hwm` across calls and
+ *              guarantees that on entry logits[b][s] == -inf for every
+ *              s >= row_hwm[b] (e.g. logits all -inf and row_hwm all 0 before
+ *              the first call); the call then rewrites -inf only on pages in
+ *              [seq_lens[b], row_hwm[b]) and sets row_hwm[b] = seq_lens[b]
+ *              (clamped). The result is identical in both modes.
+ *   stream     HIP stream to enqueue on
+ */
+int dsa_indexer_score(const void *q, const float *w, const void *k_pool, int64_t num_pages,
+                      const int32_t *page_table, const int32_t *seq_lens, int32_t batch,
+                      int32_t max_pages, float *logits, int32_t *row_hwm, hipStream_t stream);
+
+/* Bytes of device workspace dsa_indexer_topk needs for these sizes
+ * (0 means the workspace pointer may be NULL). */
+size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k);
+
+/*
+ * Top-k step (step 4 above; page "The O(Actual) Indexer", section "The
+ * Benchmark Results", on the top-k that follows the indexer): for every
+ * request b with L = clamp(seq_lens[b], 0, max_c4), picks the min(k, L)
+ * positions of logits[b][0:L] with the largest scores. Ranking: larger score
+ * first; among equal scores the lower position first (-0 and +0 are equal);
+ * NaN ranks below every number. Positions at or past L are never read.
+ *
+ *   logits     fp32  [batch][max_c4] (as written by dsa_indexer_score)
+ *   seq_lens   int32 [batch]
+ *   batch      1 .. 65535
+ *   max_c4     row width, 1 .. 2^28
+ *   k          1 .. max_c4
+ *   out_idx    int32 [batch][k]: the chosen positions in ascending order,
+ *              then -1 in the remaining k - min(k, L) slots
+ *   out_vals   NULL, or fp32 [batch][k]: logits at out_idx, NaN in padding
+ *   workspace  device buffer of ws_bytes >= dsa_indexer_topk_workspace_bytes()
+ *              (may be NULL when that is 0)
+ *   stream     HIP stream to enqueue on
+ */
+int dsa_indexer_topk(const float *logits, const int32_t *seq_lens, int32_t batch, int32_t max_c4,
+                     int32_t k, int32_t *out_idx, float *out_vals, void *workspace,
+                     size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_INDEXER_H */

@@ -1,0 +1,168 @@
+"""Thin Python binding of the C ABI in ``include/dsa_indexer.h``.
+
+Argument marshalling only: checks dtypes, shapes, devices and contiguity of
+torch tensors, passes their device pointers and the current HIP stream to the
+library, and raises ``DsaError`` on a negative status. Every step of the
+decode path runs in the library's HIP kernels; there is no fallback, and a
+missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+from . import build as _build
+
+HEADS, DIM, PAGE = 32, 64, 64
+
+_STATUS = {0: "DSA_OK", -1: "DSA_ERR_NULL", -2: "DSA_ERR_SHAPE", -3: "DSA_ERR_ALIGN",
+           -4: "DSA_ERR_K", -5: "DSA_ERR_WORKSPACE", -6: "DSA_ERR_HIP"}
+
+
+class DsaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {_STATUS.get(status, status)} ({status_string(status)})")
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _build.LIB_PATH
+
+
+def load() -> ctypes.CDLL:
+    """Load libdsa_indexer.so (building it first only if none is built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        _build.build()
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.dsa_indexer_abi_version.restype = ctypes.c_int
+    lib.dsa_indexer_abi_version.argtypes = []
+    lib.dsa_indexer_status_string.restype = ctypes.c_char_p
+    lib.dsa_indexer_status_string.argtypes = [ctypes.c_int]
+    lib.dsa_indexer_last_hip_error.restype = ctypes.c_int
+    lib.dsa_indexer_last_hip_error.argtypes = []
+    lib.dsa_indexer_score.restype = ctypes.c_int
+    lib.dsa_indexer_score.argtypes = [vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, vp]
+    lib.dsa_indexer_topk_workspace_bytes.restype = sz
+    lib.dsa_indexer_topk_workspace_bytes.argtypes = [i32, i32, i32]
+    lib.dsa_indexer_topk.restype = ctypes.c_int
+    lib.dsa_indexer_topk.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+    _lib = lib
+    return lib
+
+
+def abi_version() -> int:
+    return load().dsa_indexer_abi_version()
+
+
+def status_string(status: int) -> str:
+    return load().dsa_indexer_status_string(status).decode()
+
+
+def _stream_ptr(stream):
+    import torch
+
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _check(t, name, dtypes, shape=None, device=None):
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def score(q, w, k_pool, page_table, seq_lens, out=None, row_hwm=None, stream=None):
+    """Logits [B, max_pages*64] (float32) of one decode step.
+
+    q bf16 [B,32,64]; w float32 [B,32]; k_pool bf16 [num_pages,64,64];
+    page_table int32 [B,max_pages]; seq_lens int32 [B]; ``out`` float32
+    [B, max_pages*64] is allocated when not given; ``row_hwm`` int32 [B]
+    selects the incremental -inf tail (see the header).
+    """
+    import torch
+
+    B, S = page_table.shape
+    dev = q.device
+    bf16 = (torch.bfloat16, torch.int16)
+    _check(q, "q", bf16, (B, HEADS, DIM))
+    _check(w, "w", (torch.float32,), (B, HEADS), dev)
+    _check(k_pool, "k_pool", bf16, None, dev)
+    if k_pool.dim() != 3 or tuple(k_pool.shape[1:]) != (PAGE, DIM):
+        raise ValueError(f"k_pool has shape {tuple(k_pool.shape)}, expected [num_pages, {PAGE}, {DIM}]")
+    _check(page_table, "page_table", (torch.int32,), None, dev)
+    _check(seq_lens, "seq_lens", (torch.int32,), (B,), dev)
+    if out is None:
+        out = torch.empty((B, S * PAGE), dtype=torch.float32, device=dev)
+    _check(out, "out", (torch.float32,), (B, S * PAGE), dev)
+    if row_hwm is not None:
+        _check(row_hwm, "row_hwm", (torch.int32,), (B,), dev)
+    st = load().dsa_indexer_score(
+        q.data_ptr(), w.data_ptr(), k_pool.data_ptr(), k_pool.shape[0], page_table.data_ptr(),
+        seq_lens.data_ptr(), B, S, out.data_ptr(), row_hwm.data_ptr() if row_hwm is not None else None,
+        _stream_ptr(stream))
+    if st != 0:
+        raise DsaError(st, "dsa_indexer_score")
+    return out
+
+
+def topk_workspace_bytes(batch: int, max_c4: int, k: int) -> int:
+    return int(load().dsa_indexer_topk_workspace_bytes(batch, max_c4, k))
+
+
+def topk(logits, seq_lens, k, out_idx=None, out_vals=None, with_values=False, workspace=None,
+         stream=None):
+    """Top-k positions [B, k] (int32, ascending, -1 padded) of each row, and
+    their scores [B, k] when ``with_values`` or ``out_vals`` is given."""
+    import torch
+
+    B, N = logits.shape
+    dev = logits.device
+    _check(logits, "logits", (torch.float32,), None)
+    _check(seq_lens, "seq_lens", (torch.int32,), (B,), dev)
+    if out_idx is None:
+        out_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    _check(out_idx, "out_idx", (torch.int32,), (B, k), dev)
+    if out_vals is None and with_values:
+        out_vals = torch.empty((B, k), dtype=torch.float32, device=dev)
+    if out_vals is not None:
+        _check(out_vals, "out_vals", (torch.float32,), (B, k), dev)
+    need = topk_workspace_bytes(B, N, k)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().dsa_indexer_topk(
+        logits.data_ptr(), seq_lens.data_ptr(), B, N, k, out_idx.data_ptr(),
+        out_vals.data_ptr() if out_vals is not None else None, ws_ptr, ws_bytes, _stream_ptr(stream))
+    if st != 0:
+        raise DsaError(st, "dsa_indexer_topk")
+    return out_idx, out_vals
+
+
+def to_device(inp, device="cuda"):
+    """Upload a ``workloads.Inputs`` to the GPU as the tensors ``score`` takes."""
+    import torch
+
+    return {
+        "q": torch.from_numpy(inp.q_bits.view("int16")).to(device).view(torch.bfloat16),
+        "w": torch.from_numpy(inp.w).to(device),
+        "k_pool": torch.from_numpy(inp.k_bits.view("int16")).to(device).view(torch.bfloat16),
+        "page_table": torch.from_numpy(inp.page_table).to(device),
+        "seq_lens": torch.from_numpy(inp.seq_lens).to(device),
+    }

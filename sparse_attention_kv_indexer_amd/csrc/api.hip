@@ -1,0 +1,77 @@
+// C ABI entry points: host-side validation, then the kernel launches.
+// Nothing here allocates, synchronizes or reads device memory.
+#include "dsa_indexer.h"
+
+#include "common.h"
+
+namespace {
+
+thread_local int g_last_hip_error = 0;
+
+bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
+
+int from_hip(hipError_t e) {
+  if (e == hipSuccess) return DSA_OK;
+  g_last_hip_error = static_cast<int>(e);
+  return DSA_ERR_HIP;
+}
+
+constexpr int32_t kMaxBatch = 65535;  // grid y / x limit used by the launches
+constexpr int32_t kMaxPages = dsa::kMaxRowPositions / dsa::kPage;
+
+}  // namespace
+
+extern "C" {
+
+int dsa_indexer_abi_version(void) { return DSA_INDEXER_ABI_VERSION; }
+
+const char* dsa_indexer_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_NULL: return "a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "batch, max_pages, num_pages or max_c4 out of range";
+    case DSA_ERR_ALIGN: return "a pointer misses its required alignment";
+    case DSA_ERR_K: return "k out of [1, max_c4]";
+    case DSA_ERR_WORKSPACE: return "workspace too small";
+    case DSA_ERR_HIP: return "HIP runtime error on launch";
+    default: return "unknown status";
+  }
+}
+
+int dsa_indexer_last_hip_error(void) { return g_last_hip_error; }
+
+int dsa_indexer_score(const void* q, const float* w, const void* k_pool, int64_t num_pages,
+                      const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
+                      int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream) {
+  if (!q || !w || !k_pool || !page_table || !seq_lens || !logits) return DSA_ERR_NULL;
+  if (batch < 1 || batch > kMaxBatch || max_pages < 1 || max_pages > kMaxPages || num_pages < 1)
+    return DSA_ERR_SHAPE;
+  if (misaligned16(q) || misaligned16(w) || misaligned16(k_pool) || misaligned16(logits) ||
+      misaligned4(page_table) || misaligned4(seq_lens) || misaligned4(row_hwm))
+    return DSA_ERR_ALIGN;
+  return from_hip(dsa::launch_score(q, w, k_pool, num_pages, page_table, seq_lens, batch, max_pages,
+                                    logits, row_hwm, stream));
+}
+
+size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k) {
+  (void)batch;
+  (void)max_c4;
+  (void)k;
+  return 0;
+}
+
+int dsa_indexer_topk(const float* logits, const int32_t* seq_lens, int32_t batch, int32_t max_c4,
+                     int32_t k, int32_t* out_idx, float* out_vals, void* workspace, size_t ws_bytes,
+                     hipStream_t stream) {
+  if (!logits || !seq_lens || !out_idx) return DSA_ERR_NULL;
+  if (batch < 1 || batch > kMaxBatch || max_c4 < 1 || max_c4 > dsa::kMaxRowPositions) return DSA_ERR_SHAPE;
+  if (k < 1 || k > max_c4) return DSA_ERR_K;
+  const size_t need = dsa_indexer_topk_workspace_bytes(batch, max_c4, k);
+  if (ws_bytes < need || (need > 0 && workspace == nullptr)) return DSA_ERR_WORKSPACE;
+  if (misaligned4(logits) || misaligned4(seq_lens) || misaligned4(out_idx) || misaligned4(out_vals))
+    return DSA_ERR_ALIGN;
+  return from_hip(dsa::launch_topk(logits, seq_lens, batch, max_c4, k, out_idx, out_vals, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,47 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+constexpr int kHeads = 32;            // indexer heads
+constexpr int kDim = 64;              // head dimension
+constexpr int kPage = 64;             // c4 positions per page
+constexpr int kRowBytes = kDim * 2;   // one bf16 key: 128 B
+constexpr int kPageBytes = kPage * kRowBytes;  // 8 KiB
+constexpr int kPageChunks = kPageBytes / 16;   // 512 chunks of 16 B
+
+typedef __bf16 bf16x8 __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Device memory is reached through raw buffer resources: a wave-uniform base
+// and byte range in SGPRs plus a 32-bit per-lane byte offset. No per-lane
+// 64-bit address is ever formed, and the hardware drops (or reads as 0) any
+// access at or past the resource's range instead of touching other memory.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRawBufferFlags = 0x00020000;  // dword 3 of a raw CDNA buffer descriptor
+constexpr int kNonTemporal = 2;              // cache policy: streaming, read once
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           kRawBufferFlags);
+}
+
+// Largest row width (positions) either kernel accepts: keeps every row's
+// byte range inside one 32-bit buffer range.
+constexpr int32_t kMaxRowPositions = 1 << 28;
+
+// Enqueue the score kernel (and, with row_hwm, the high-water-mark update).
+hipError_t launch_score(const void* q, const float* w, const void* k_pool, int64_t num_pages,
+                        const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
+                        int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream);
+
+// Enqueue the top-k kernel.
+hipError_t launch_topk(const float* logits, const int32_t* seq_lens, int32_t batch, int32_t max_c4,
+                       int32_t k, int32_t* out_idx, float* out_vals, hipStream_t stream);
+
+}  // namespace dsa

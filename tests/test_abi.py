@@ -1,0 +1,96 @@
+"""The C ABI without a GPU: the library loads, exports every function the
+header declares, and rejects bad arguments on the host with the documented
+status codes before any HIP call (every call below fails validation, so
+nothing is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from sparse_attention_kv_indexer_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "dsa_indexer.h")
+
+OK, NULL, SHAPE, ALIGN, K, WS = 0, -1, -2, -3, -4, -5
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(dsa_indexer_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return binding.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 6, names
+    for name in names:
+        assert hasattr(lib, name), f"{name} not exported"
+
+
+def test_version_and_status_strings(lib):
+    assert lib.dsa_indexer_abi_version() == 1
+    for st in (OK, NULL, SHAPE, ALIGN, K, WS, -6):
+        assert lib.dsa_indexer_status_string(st).decode() not in ("", "unknown status")
+    assert lib.dsa_indexer_status_string(12345).decode() == "unknown status"
+    assert lib.dsa_indexer_last_hip_error() == 0
+
+
+A = 1 << 20  # a 16-byte aligned stand-in address; never dereferenced (validation fails first)
+
+
+def score_args(**over):
+    args = dict(q=A, w=A, k_pool=A, num_pages=4, page_table=A, seq_lens=A, batch=2, max_pages=3,
+                logits=A, row_hwm=None, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("field", ["q", "w", "k_pool", "page_table", "seq_lens", "logits"])
+def test_score_null(lib, field):
+    assert lib.dsa_indexer_score(*score_args(**{field: None}, batch=0)) == NULL
+
+
+@pytest.mark.parametrize("over", [dict(batch=0), dict(batch=-1), dict(batch=65536), dict(max_pages=0),
+                                  dict(max_pages=(1 << 22) + 1), dict(num_pages=0), dict(num_pages=-3)])
+def test_score_shape(lib, over):
+    assert lib.dsa_indexer_score(*score_args(**over)) == SHAPE
+
+
+@pytest.mark.parametrize("field,off", [("q", 8), ("w", 4), ("k_pool", 2), ("logits", 4), ("page_table", 2),
+                                       ("seq_lens", 1), ("row_hwm", 2)])
+def test_score_alignment(lib, field, off):
+    assert lib.dsa_indexer_score(*score_args(**{field: A + off})) == ALIGN
+
+
+def topk_args(**over):
+    args = dict(logits=A, seq_lens=A, batch=2, max_c4=128, k=16, out_idx=A, out_vals=None,
+                workspace=None, ws_bytes=0, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("field", ["logits", "seq_lens", "out_idx"])
+def test_topk_null(lib, field):
+    assert lib.dsa_indexer_topk(*topk_args(**{field: None})) == NULL
+
+
+@pytest.mark.parametrize("over,want", [(dict(batch=0), SHAPE), (dict(max_c4=0), SHAPE), (dict(batch=70000), SHAPE), (dict(max_c4=(1 << 28) + 1, k=1), SHAPE),
+                                       (dict(k=0), K), (dict(k=-2), K), (dict(k=129), K),
+                                       (dict(out_idx=A + 2), ALIGN), (dict(out_vals=A + 1), ALIGN),
+                                       (dict(logits=A + 3), ALIGN)])
+def test_topk_rejects(lib, over, want):
+    assert lib.dsa_indexer_topk(*topk_args(**over)) == want
+
+
+def test_topk_workspace_contract(lib):
+    need = lib.dsa_indexer_topk_workspace_bytes(64, 32768, 2048)
+    assert need >= 0
+    if need > 0:
+        assert lib.dsa_indexer_topk(*topk_args(ws_bytes=need - 1, workspace=A, k=0)) in (K, WS)

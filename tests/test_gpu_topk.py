@@ -1,0 +1,95 @@
+"""Parity of the HIP top-k kernel (GPU): bit-exact against the oracle's top-k
+on the same float32 scores, and against the oracle's float64 scores up to the
+near-tie band."""
+import numpy as np
+import pytest
+
+from gpu_helpers import check_topk_exact, oracle_scores, run_score, run_topk, say
+from sparse_attention_kv_indexer_amd import workloads as wl
+from tolerance import check_topk_cross
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("name", ["tiny", "c2", "stress8k", "stress1m", "c3", "full"])
+def test_workload_topk(lib, name):
+    say(f"topk parity {name}")
+    inp = wl.generate(name)
+    got, t, out = run_score(lib, inp)
+    idx, vals = run_topk(lib, out, t["seq_lens"], inp.topk)
+    check_topk_exact(idx, vals, got, inp.seq_lens, inp.topk)
+    ref, M, A = oracle_scores(inp)
+    check_topk_cross(idx, ref, M, A, inp.seq_lens, inp.topk)
+
+
+def _upload(x, lens):
+    import torch
+
+    return (torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda(),
+            torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda())
+
+
+@pytest.mark.parametrize("k", [1, 5, 64, 1000, 1024, 1025, 4096])
+def test_random_rows(lib, k):
+    rng = np.random.default_rng(k)
+    B, N = 12, 5000
+    x = rng.standard_normal((B, N)).astype(np.float32)
+    lens = np.array([0, 1, k - 1, k, k + 1, 1023, 1024, 1025, 4999, 5000, 3000, 77])
+    lens = np.clip(lens, 0, N)
+    say(f"topk random rows k={k}")
+    xd, ld = _upload(x, lens)
+    idx, vals = run_topk(lib, xd, ld, k)
+    check_topk_exact(idx, vals, x, lens, k)
+
+
+def test_heavy_ties_signed_zero_nan_inf(lib):
+    rng = np.random.default_rng(5)
+    B, N, k = 6, 3000, 700
+    x = rng.integers(-3, 4, size=(B, N)).astype(np.float32)  # 7 distinct values: ties everywhere
+    x[1] = 0.0
+    x[1, ::3] = -0.0                      # -0 and +0 tie
+    x[2, :] = 1.5                          # all equal
+    x[3, 10:2000:7] = np.nan               # NaN ranks last
+    x[4, ::5] = -np.inf
+    x[5, :] = np.nan
+    lens = np.array([3000, 3000, 2999, 3000, 2500, 1500])
+    say("topk ties/zeros/nan/inf")
+    xd, ld = _upload(x, lens)
+    idx, vals = run_topk(lib, xd, ld, k)
+    check_topk_exact(idx, vals, x, lens, k)
+    assert idx[2].tolist() == list(range(k))
+    assert idx[5].tolist() == list(range(k))
+
+
+def test_long_rows_beyond_lds(lib):
+    """Rows longer than the keys the kernel keeps in LDS re-read the logits."""
+    rng = np.random.default_rng(6)
+    B, N, k = 3, 70000, 2048
+    x = rng.standard_normal((B, N)).astype(np.float32)
+    x[2] = np.round(x[2] * 4) / 4  # ties across a long row
+    lens = np.array([70000, 40000, 65537])
+    say("topk long rows")
+    xd, ld = _upload(x, lens)
+    idx, vals = run_topk(lib, xd, ld, k)
+    check_topk_exact(idx, vals, x, lens, k)
+
+
+def test_k_equals_row_width(lib):
+    x = np.random.default_rng(7).standard_normal((2, 64)).astype(np.float32)
+    lens = np.array([64, 30])
+    say("topk k = row width")
+    xd, ld = _upload(x, lens)
+    idx, vals = run_topk(lib, xd, ld, 64)
+    check_topk_exact(idx, vals, x, lens, 64)
+    assert idx[0].tolist() == list(range(64))
+    assert idx[1].tolist() == list(range(30)) + [-1] * 34
+
+
+def test_without_values(lib):
+    x = np.random.default_rng(8).standard_normal((4, 1000)).astype(np.float32)
+    lens = np.array([1000, 999, 500, 10])
+    say("topk no values")
+    xd, ld = _upload(x, lens)
+    idx, vals = run_topk(lib, xd, ld, 100, with_values=False)
+    assert vals is None
+    check_topk_exact(idx, None, x, lens, 100)
