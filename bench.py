@@ -1,0 +1,248 @@
+"""Decode-step benchmark of the DSA indexer on one MI355X.
+
+A step is the whole hot path over one batch: the score kernel (page walk,
+weighted-ReLU scores, -inf tail) followed by the top-k kernel, both replayed
+from a captured HIP graph. Inputs are seeded synthetic tensors already
+resident in HBM; R identical copies at different addresses are used round
+robin so that every step reads its keys from HBM, not from the 256 MB
+Infinity Cache.
+
+Prints one JSON line. ``value`` is valid positions scored per second over the
+timed steps; ``roofline`` prices the score kernel's algorithmic bytes per
+launch against the 8 TB/s HBM peak, using its average launch duration
+measured here with HIP events; ``cpu_baseline`` times the float64 CPU oracle
+on the host cores over a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
+MALL_BYTES = 256 << 20  # Infinity Cache
+METRIC = "valid positions scored/s + µs/step at B=64,128K ctx; % of HBM roofline"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
+SCORE_SOURCES = ["sparse_attention_kv_indexer_amd/csrc/score.hip", "sparse_attention_kv_indexer_amd/csrc/common.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c3", help="workload name (tiny, c2, c3, stress1m, stress8k, full)")
+    ap.add_argument("--rotate", type=int, default=0, help="input copies used round robin (0: enough to exceed 2x the Infinity Cache)")
+    ap.add_argument("--hwm", action="store_true", help="incremental -inf tail (row_hwm) instead of the stateless full tail")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-reps", type=int, default=3)
+    return ap.parse_args()
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for rel in SCORE_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def algorithmic_bytes(inp, hwm: bool) -> dict:
+    """Bytes one score launch must move at minimum: every valid key row, the
+    logits it writes, the page-table entries of valid slots, and q, w and the
+    length of every request."""
+    import numpy as np
+
+    from sparse_attention_kv_indexer_amd import workloads as wl
+
+    lens = np.clip(inp.seq_lens.astype(np.int64), 0, inp.max_c4)
+    pages = wl.pages_needed(lens)
+    k_bytes = int(pages.sum()) * wl.PAGE * wl.DIM * 2
+    out_positions = inp.batch * inp.max_c4 if not hwm else int((pages * wl.PAGE).sum())
+    out_bytes = out_positions * 4
+    table_bytes = int(pages.sum()) * 4
+    req_bytes = inp.batch * (wl.HEADS * wl.DIM * 2 + wl.HEADS * 4 + 4)
+    return {"k": k_bytes, "logits": out_bytes, "page_table": table_bytes, "q_w_len": req_bytes,
+            "total": k_bytes + out_bytes + table_bytes + req_bytes}
+
+
+def cpu_baseline(inp, reps: int) -> dict:
+    """The oracle, as it stands, on the host: score + top-k of the whole step
+    when it fits the time budget, else of the first requests."""
+    import numpy as np
+
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # threadpoolctl missing: numpy's BLAS default is one thread per core
+        threads = os.cpu_count() or 1
+    rows = inp.batch
+    budget_s = 10.0
+    times = []
+    for _ in range(max(reps, 1)):
+        sub = inp
+        if rows < inp.batch:
+            sub = type(inp)(inp.q_bits[:rows], inp.w[:rows], inp.k_bits, inp.page_table[:rows],
+                            inp.seq_lens[:rows], inp.topk)
+        t0 = time.perf_counter()
+        s = oracle.score(sub.q_bits, sub.w, sub.k_bits, sub.page_table, sub.seq_lens)
+        oracle.topk(s, sub.seq_lens, sub.topk)
+        dt = time.perf_counter() - t0
+        times.append(dt)
+        if dt > budget_s and rows > 1:  # shrink the sample for the remaining repetitions
+            rows = max(1, int(rows * budget_s / dt))
+            times = []
+    dt = sorted(times)[len(times) // 2]
+    valid = int(np.clip(inp.seq_lens[:rows], 0, inp.max_c4).sum())
+    try:
+        cpu = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")][0]
+    except Exception:
+        cpu = "unknown"
+    return {"value": valid / dt, "unit": "valid positions/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"score + top-{inp.topk} of {rows} of {inp.batch} requests ({valid} valid positions), "
+                      f"float64 numpy oracle, median of {len(times)}, {dt:.3f} s each; cpu {cpu}"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU only (no cross-GPU sharding or collectives); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sparse_attention_kv_indexer_amd import binding, workloads as wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    binding.load()
+    cfg = wl.CONFIGS[args.config]
+    inp = wl.generate(cfg)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    base = binding.to_device(inp, dev)
+    B, N, k = inp.batch, inp.max_c4, inp.topk
+    set_bytes = inp.k_bits.nbytes + B * N * 4
+    R = args.rotate or min(16, max(2, math.ceil(2 * MALL_BYTES / set_bytes)))
+    sets = []
+    for r in range(R):
+        t = {name: (v if r == 0 else v.clone()) for name, v in base.items()}
+        t["logits"] = torch.full((B, N), float("-inf"), dtype=torch.float32, device=dev)
+        t["hwm"] = torch.zeros(B, dtype=torch.int32, device=dev) if args.hwm else None
+        t["idx"] = torch.empty((B, k), dtype=torch.int32, device=dev)
+        t["vals"] = torch.empty((B, k), dtype=torch.float32, device=dev)
+        sets.append(t)
+
+    def launch_score(t):
+        binding.score(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"], out=t["logits"],
+                      row_hwm=t["hwm"])
+
+    def launch_topk(t):
+        binding.topk(t["logits"], t["seq_lens"], k, out_idx=t["idx"], out_vals=t["vals"])
+
+    # warm up eagerly once per set (also brings row_hwm to its steady state)
+    for t in sets:
+        launch_score(t)
+        launch_topk(t)
+    torch.cuda.synchronize()
+
+    # one captured graph per input copy: [score; top-k]
+    graphs = []
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    for t in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            launch_score(t)
+            launch_topk(t)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(args.steps):
+        graphs[i % R].replay()
+    end.record()
+    torch.cuda.synchronize()
+    ms_per_step = start.elapsed_time(end) / args.steps
+
+    # average launch duration of each kernel: n launches queued back to back on
+    # the launching stream behind a spin kernel (so the host never starves the
+    # GPU), bracketed by one pair of HIP events
+    def per_launch_ms(fn, n):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(2.4e9 * 0.02))  # ~20 ms of queued work ahead of the launches
+        s.record()
+        for i in range(n):
+            fn(sets[i % R])
+        e.record()
+        torch.cuda.synchronize()
+        return s.elapsed_time(e) / n
+
+    n_kern = max(10, min(args.steps, 200))
+    score_avg_ms = per_launch_ms(launch_score, n_kern)
+    topk_avg_ms = per_launch_ms(launch_topk, n_kern)
+
+    valid = int(np.clip(inp.seq_lens, 0, N).sum())
+    alg = algorithmic_bytes(inp, args.hwm)
+    achieved = alg["total"] / (score_avg_ms * 1e-3) / 1e9
+    k_only = alg["k"] / (score_avg_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        rec = json.load(open(TRAFFIC_FILE)).get(args.config + ("+hwm" if args.hwm else ""))
+        if rec and rec.get("source_digest") == source_digest():
+            traffic = rec["bytes_per_launch"]
+    roofline = {
+        "bound": "hbm", "kernel": "score_kernel", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+        "algorithmic_bytes_per_launch": alg, "launch_avg_us": round(score_avg_ms * 1e3, 3),
+        "k_bytes_only": {"achieved": round(k_only, 1), "frac": round(k_only / HBM_PEAK_GBS, 4)},
+        "topk_launch_avg_us": round(topk_avg_ms * 1e3, 3),
+    }
+    result = {
+        "metric": METRIC,
+        "value": valid / (ms_per_step * 1e-3),
+        "unit": "valid positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "us_per_step": ms_per_step * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.description}",
+            "batch": B, "heads": wl.HEADS, "dim": wl.DIM, "page_positions": wl.PAGE, "max_pages": inp.max_pages,
+            "max_c4": N, "valid_positions": valid, "valid_pages": int(wl.pages_needed(inp.seq_lens).sum()),
+            "topk": k, "seed": cfg.seed, "tail": "incremental (row_hwm)" if args.hwm else "stateless full -inf",
+            "input_copies": R, "timing": "hipGraph replay of [score; top-k], HIP events",
+            "accumulate": "fp32",
+        },
+        "roofline": roofline,
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu:
+        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_reps)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -93,3 +93,23 @@ def test_without_values(lib):
     idx, vals = run_topk(lib, xd, ld, 100, with_values=False)
     assert vals is None
     check_topk_exact(idx, None, x, lens, 100)
+
+
+def test_sampled_cut_fallbacks(lib):
+    """Rows longer than the candidate capacity whose sampled cut cannot be
+    used: all keys equal (too many candidates), and large scores placed
+    exactly where one key per 32 is sampled (too few keys above the cut)."""
+    B, N = 3, 32768
+    x = np.zeros((B, N), np.float32)
+    x[0, :] = 0.75
+    rng = np.random.default_rng(9)
+    x[1] = rng.standard_normal(N).astype(np.float32)
+    t = np.arange(1024)
+    x[1, 32 * t + (t & 31)] = 100.0 + rng.random(1024).astype(np.float32)  # every sampled slot is huge
+    x[2] = np.round(rng.standard_normal(N) * 2).astype(np.float32)  # a handful of distinct values
+    lens = np.array([20000, 32768, 30001])
+    for k in (100, 2048, 5000):
+        say(f"topk sampled-cut fallbacks k={k}")
+        xd, ld = _upload(x, lens)
+        idx, vals = run_topk(lib, xd, ld, k)
+        check_topk_exact(idx, vals, x, lens, k)
