@@ -29,7 +29,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
 MALL_BYTES = 256 << 20  # Infinity Cache
 METRIC = "valid positions scored/s + µs/step at B=64,128K ctx; % of HBM roofline"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.txt")
 SCORE_SOURCES = ["sparse_attention_kv_indexer_amd/csrc/score.hip", "sparse_attention_kv_indexer_amd/csrc/common.h"]
 
 
@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--hwm", action="store_true", help="incremental -inf tail (row_hwm) instead of the stateless full tail")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain device-to-device copy of known size (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -52,6 +54,37 @@ def source_digest() -> str:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
+
+
+def read_traffic(key: str):
+    """HBM bytes per score launch measured with rocprofv3 counters, from the
+    summary under profiles/, or None when absent or taken on other source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    for line in open(TRAFFIC_FILE):
+        line = line.strip()
+        if line.startswith(key + " "):
+            rec = dict(kv.split("=", 1) for kv in line.split()[1:])
+    if rec.get("source_digest") != source_digest():
+        return None
+    return {"read_bytes": int(rec["read_bytes"]), "write_bytes": int(rec["write_bytes"]),
+            "total_bytes": int(rec["read_bytes"]) + int(rec["write_bytes"])}
+
+
+def copy_calibration():
+    """A plain copy of 512 MiB, five times: the reference that scales the HBM
+    byte counters (FETCH_SIZE / WRITE_SIZE) to bytes."""
+    import torch
+
+    n = 512 << 20
+    src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
 
 
 def algorithmic_bytes(inp, hwm: bool) -> dict:
@@ -126,6 +159,9 @@ def main():
     from sparse_attention_kv_indexer_amd import binding, workloads as wl
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration()
+        return
     binding.load()
     cfg = wl.CONFIGS[args.config]
     inp = wl.generate(cfg)
@@ -202,11 +238,7 @@ def main():
     alg = algorithmic_bytes(inp, args.hwm)
     achieved = alg["total"] / (score_avg_ms * 1e-3) / 1e9
     k_only = alg["k"] / (score_avg_ms * 1e-3) / 1e9
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        rec = json.load(open(TRAFFIC_FILE)).get(args.config + ("+hwm" if args.hwm else ""))
-        if rec and rec.get("source_digest") == source_digest():
-            traffic = rec["bytes_per_launch"]
+    traffic = read_traffic(args.config + ("+hwm" if args.hwm else ""))
     roofline = {
         "bound": "hbm", "kernel": "score_kernel", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
