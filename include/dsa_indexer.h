@@ -88,7 +88,8 @@ int dsa_indexer_last_hip_error(void);
  *              s of request b lives in page page_table[b][s / 64], row s % 64
  *   seq_lens   int32 [batch]: valid c4 positions per request
  *   batch      1 .. 65535
- *   max_pages  1 .. 2^22 (row width max_pages * 64 at most 2^28 positions)
+ *   max_pages  1 .. 2^22 (row width max_pages * 64 at most 2^28 positions),
+ *              with batch * max_pages at most 2^26 (at most 2^32 logits)
  *   logits     fp32  [batch][max_pages*64], 16-byte aligned; on return of the
  *              enqueued work: the score for s < seq_lens[b], -inf otherwise
  *              (bit pattern 0xFF800000)

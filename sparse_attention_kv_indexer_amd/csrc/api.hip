@@ -19,6 +19,7 @@ int from_hip(hipError_t e) {
 
 constexpr int32_t kMaxBatch = 65535;  // grid y / x limit used by the launches
 constexpr int32_t kMaxPages = dsa::kMaxRowPositions / dsa::kPage;
+constexpr int64_t kMaxSlots = int64_t(1) << 26;  // batch * max_pages: at most 2^32 logits
 
 }  // namespace
 
@@ -45,7 +46,8 @@ int dsa_indexer_score(const void* q, const float* w, const void* k_pool, int64_t
                       const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
                       int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream) {
   if (!q || !w || !k_pool || !page_table || !seq_lens || !logits) return DSA_ERR_NULL;
-  if (batch < 1 || batch > kMaxBatch || max_pages < 1 || max_pages > kMaxPages || num_pages < 1)
+  if (batch < 1 || batch > kMaxBatch || max_pages < 1 || max_pages > kMaxPages || num_pages < 1 ||
+      (int64_t)batch * max_pages > kMaxSlots)
     return DSA_ERR_SHAPE;
   if (misaligned16(q) || misaligned16(w) || misaligned16(k_pool) || misaligned16(logits) ||
       misaligned4(page_table) || misaligned4(seq_lens) || misaligned4(row_hwm))

@@ -7,25 +7,38 @@
 // and -inf at every position at or past the length, over a row of
 // max_pages * 64 positions.
 //
-// Launch shape: one 64-lane workgroup per (page slot, request), a grid fixed by
-// (max_pages, batch) so the launch can be captured once and replayed for any
-// lengths. A workgroup whose slot lies wholly past the length takes the early
-// exit of the section "The Benchmark Results": it reads neither the page table
-// nor the key page and only writes 64 x -inf (or nothing, in the incremental
-// mode, when the page is already -inf). Work and HBM traffic therefore follow
-// the actual length; only the 4-byte output per position follows the row width.
+// Work list. The work of one call is a flat list: first every valid page of
+// every request (request-major, page-minor), then the -inf tail of every
+// request cut into chunks of kTailChunk positions. The tail of a request runs
+// from its first page past the length to the row end (stateless mode) or to
+// the page holding its previous high-water mark (incremental mode, where
+// everything beyond is -inf already). A fixed grid of one-wave workgroups, as
+// many as the chip keeps resident (capped by the largest list the shapes
+// allow), splits the list into equal contiguous ranges. The launch shape
+// depends only on (batch, max_pages), so it can be captured once and replayed
+// for any lengths, and the work and HBM traffic follow the actual lengths:
+// pages past a length are never read (the early exit of the section "The
+// Benchmark Results"), and in the incremental mode the tail is not rewritten.
+// Each workgroup finds the requests its range starts in with wave scans over
+// windows of 64 request lengths, walks its range in order, loads q and w only
+// when the request changes, and prefetches the next page while it computes
+// the current one.
 //
-// A valid slot reads its 8 KiB key page with eight fully coalesced 1 KiB wave
-// loads, stages it in LDS under an XOR swizzle, and contracts it against the
-// request's 32 x 64 query block with eight v_mfma_f32_32x32x16_bf16 (bf16
-// products, fp32 accumulation). The accumulator holds the 32 heads x 32
-// positions of each half page with one position per lane; ReLU, the head
-// weights and 16 of the 32 heads are summed in registers, and one cross-half
-// lane exchange adds the other 16 heads.
+// A page is read with eight fully coalesced 1 KiB wave loads, staged in LDS
+// under an XOR swizzle, and contracted against the request's 32 x 64 query
+// block with eight v_mfma_f32_32x32x16_bf16 (bf16 products, fp32
+// accumulation). The accumulator holds the 32 heads x 32 positions of each
+// half page with one position per lane; ReLU, the head weights and 16 of the
+// 32 heads are summed in registers, and one cross-half lane exchange adds the
+// other 16 heads. The tail is written with 16-byte stores, 1 KiB per wave
+// instruction.
 #include "common.h"
 
 namespace dsa {
 namespace {
+
+constexpr int kTailChunk = 4096;  // positions per tail item (16 KiB of -inf)
+constexpr int kWavesPerCU = 12;   // resident one-wave workgroups per CU at this kernel's registers
 
 __device__ __forceinline__ int clamp_len(int len, int width) { return min(max(len, 0), width); }
 
@@ -34,6 +47,80 @@ __device__ __forceinline__ int clamp_len(int len, int width) { return min(max(le
 // consecutive lanes of an MFMA operand load on distinct banks.
 __device__ __forceinline__ int lds_slot(int row, int col) { return row * 8 + (col ^ (row & 7)); }
 
+// Inclusive scan over the 64 lanes of a wave (row shifts, then row broadcasts).
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_total(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(v), 63);
+}
+
+struct Shape {
+  rsrc_t lens;   // int32 [batch]
+  rsrc_t marks;  // int32 [batch] high-water marks, if `incremental`
+  bool incremental;
+  int batch, width;
+};
+
+// Request b's share of the work: its valid pages, and the positions
+// [tail0, tail1) of its -inf tail in chunks of kTailChunk.
+struct RowWork {
+  uint32_t pages, chunks, tail0, tail1;
+};
+__device__ __forceinline__ RowWork row_work(const Shape& sh, int b) {
+  RowWork r{0, 0, 0, 0};
+  if (b < sh.batch) {
+    const int len = clamp_len((int)__builtin_amdgcn_raw_buffer_load_b32(sh.lens, b * 4, 0, 0), sh.width);
+    r.pages = (uint32_t)((len + kPage - 1) / kPage);
+    r.tail0 = r.pages * kPage;
+    r.tail1 = (uint32_t)sh.width;
+    if (sh.incremental) {
+      // beyond the page holding the old mark everything is -inf already
+      const uint32_t hw =
+          (uint32_t)clamp_len((int)__builtin_amdgcn_raw_buffer_load_b32(sh.marks, b * 4, 0, 0), sh.width);
+      r.tail1 = max(r.tail0, (hw + kPage - 1) / kPage * kPage);
+    }
+    r.chunks = (r.tail1 - r.tail0 + kTailChunk - 1) / kTailChunk;
+  }
+  return r;
+}
+
+// A window of 64 requests over one of the two lists (pages or tail chunks):
+// this lane's request count, its exclusive prefix inside the window, the
+// window total, and the items before the window.
+struct Window {
+  int b0;
+  uint32_t cnt, pre, tot, acc;
+};
+__device__ __forceinline__ void window_load(Window& W, const Shape& sh, bool tail) {
+  const RowWork r = row_work(sh, W.b0 + (int)(threadIdx.x & 63));
+  W.cnt = tail ? r.chunks : r.pages;
+  const uint32_t incl = wave_inclusive_scan(W.cnt);
+  W.pre = incl - W.cnt;
+  W.tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+}
+// Moves W forward to the window holding `item` (an index into its list, below
+// the list total) and returns the request and the index inside the request.
+__device__ __forceinline__ void window_find(Window& W, uint32_t item, const Shape& sh, bool tail, int& b,
+                                            uint32_t& j) {
+  while (item >= W.acc + W.tot && W.b0 + 64 < sh.batch) {
+    W.acc += W.tot;
+    W.b0 += 64;
+    window_load(W, sh, tail);
+  }
+  const uint32_t r = item - W.acc;
+  const uint64_t m = __ballot(W.cnt > 0 && W.pre + W.cnt > r);
+  const int l = m ? __builtin_ctzll(m) : 0;  // never empty for an item below the list total
+  b = min(W.b0 + l, sh.batch - 1);
+  j = r - (uint32_t)__builtin_amdgcn_readlane((int)W.pre, l);
+}
+
 __global__ __launch_bounds__(64) void score_kernel(
     const uint16_t* __restrict__ q,          // bf16 [B][32][64]
     const float* __restrict__ w,             // [B][32]
@@ -41,91 +128,142 @@ __global__ __launch_bounds__(64) void score_kernel(
     int64_t num_pages,
     const int32_t* __restrict__ page_table,  // [B][max_pages]
     const int32_t* __restrict__ seq_lens,    // [B]
-    int32_t max_pages,
+    int32_t batch, int32_t max_pages,
     float* __restrict__ logits,              // [B][max_pages * 64]
     const int32_t* __restrict__ row_hwm)     // [B] or null
 {
-  const int slot = blockIdx.x;
-  const int b = blockIdx.y;
   const int lane = threadIdx.x;
-  const int width = max_pages * kPage;
-  const int len = clamp_len(seq_lens[b], width);
-  const int base = slot * kPage;
-  const rsrc_t out = make_rsrc(logits + (int64_t)b * width + base, kPage * sizeof(float));
+  const int half = lane >> 5;
+  const int n = lane & 31;
+  const Shape sh{make_rsrc(seq_lens, (uint32_t)batch * 4u),
+                 make_rsrc(row_hwm != nullptr ? row_hwm : seq_lens, (uint32_t)batch * 4u), row_hwm != nullptr,
+                 batch, max_pages * kPage};
 
-  float val = -__builtin_inff();
-  if (base >= len) {
-    // early exit: the whole page is past the length; no page-table or key read
-    if (row_hwm != nullptr && base >= clamp_len(row_hwm[b], width)) return;  // already -inf
-  } else {
-    const int page = page_table[(int64_t)b * max_pages + slot];
-    if (page < 0 || (int64_t)page >= num_pages) {
-      // a page id outside the pool is never dereferenced
-      val = __builtin_nanf("");
-    } else {
-      // key page: 16-byte chunk c = 64 * i + lane is key row c / 8, column c % 8;
-      // each i is one fully coalesced 1 KiB wave load
-      const rsrc_t kp = make_rsrc(k_pool + (int64_t)page * (kPage * kDim), kPageBytes);
-      u32x4 v[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        v[i] = __builtin_amdgcn_raw_buffer_load_b128(kp, (i * 64 + lane) * 16, 0, kNonTemporal);
-
-      // query operand A (32 heads x 16 dims per step): lane holds head lane%32,
-      // dims 16*kb + 8*(lane/32) .. +7 = chunk 2*kb + lane/32 of that head's row
-      const int half = lane >> 5;
-      const int n = lane & 31;
-      const rsrc_t qr = make_rsrc(q + (int64_t)b * (kHeads * kDim), kHeads * kRowBytes);
-      bf16x8 a[4];
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-        a[kb] = __builtin_bit_cast(
-            bf16x8, __builtin_amdgcn_raw_buffer_load_b128(qr, n * kRowBytes + (2 * kb + half) * 16, 0, 0));
-
-      // head weights in accumulator order: register r of a lane holds head
-      // 8*(r/4) + 4*half + r%4, so group g = r/4 is the float4 at head 8*g + 4*half
-      const rsrc_t wr = make_rsrc(w + (int64_t)b * kHeads, kHeads * sizeof(float));
-      f32x4 wv[4];
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        wv[g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, (8 * g + 4 * half) * 4, 0, 0));
-
-      __shared__ u32x4 tile[kPageChunks];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) tile[lds_slot(i * 8 + (lane >> 3), lane & 7)] = v[i];
-      __syncthreads();
-
-      // keys operand B (16 dims x 32 positions per step): lane holds position
-      // lane%32 of the half page, dims 16*kb + 8*half .. +7
-      f32x16 acc0 = {};  // positions 0..31 of the page
-      f32x16 acc1 = {};  // positions 32..63
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int col = 2 * kb + half;
-        const bf16x8 b0 = __builtin_bit_cast(bf16x8, tile[lds_slot(n, col)]);
-        const bf16x8 b1 = __builtin_bit_cast(bf16x8, tile[lds_slot(n + 32, col)]);
-        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b1, acc1, 0, 0, 0);
-      }
-
-      // weighted ReLU over this lane's 16 heads, then the other 16 from lane ^ 32
-      float p0 = 0.f, p1 = 0.f;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          p0 = __builtin_fmaf(wv[g][e], __builtin_fmaxf(acc0[4 * g + e], 0.f), p0);
-          p1 = __builtin_fmaf(wv[g][e], __builtin_fmaxf(acc1[4 * g + e], 0.f), p1);
-        }
-      }
-      p0 += __shfl_xor(p0, 32);
-      p1 += __shfl_xor(p1, 32);
-      // lane < 32 owns position lane of the first half, lane >= 32 position lane of the second
-      val = half ? p1 : p0;
-    }
-    if (base + lane >= len) val = -__builtin_inff();  // partial last page
+  // list totals, then this workgroup's contiguous range [s, e)
+  uint32_t n_pages = 0, n_chunks = 0;
+  for (int b0 = 0; b0 < batch; b0 += 64) {
+    const RowWork r = row_work(sh, b0 + lane);
+    n_pages += wave_total(r.pages);
+    n_chunks += wave_total(r.chunks);
   }
-  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), out, lane * 4, 0, 0);
+  const uint32_t total = n_pages + n_chunks;
+  const uint32_t per = (total + gridDim.x - 1) / gridDim.x;
+  const uint32_t s = blockIdx.x * per, e = min(total, s + per);
+  if (s >= e) return;
+
+  __shared__ u32x4 tile[kPageChunks];
+  if (s < n_pages) {
+    const uint32_t pe = min(e, n_pages);
+    Window W{0, 0, 0, 0, 0};
+    window_load(W, sh, false);
+    int b;
+    uint32_t j;
+    window_find(W, s, sh, false, b, j);
+
+    // key page of (request bb, slot jj) into dst; false if its id is outside the pool
+    auto fetch = [&](int bb, uint32_t jj, u32x4 (&dst)[8]) -> bool {
+      const int page = page_table[(int64_t)bb * max_pages + jj];
+      if (page < 0 || (int64_t)page >= num_pages) return false;  // never dereferenced
+      const rsrc_t kp = make_rsrc(k_pool + (int64_t)page * (kPage * kDim), kPageBytes);
+      // 16-byte chunk c = 64 * i + lane is key row c / 8, column c % 8
+#pragma unroll
+      for (int i = 0; i < 8; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b128(kp, (i * 64 + lane) * 16, 0, kNonTemporal);
+      return true;
+    };
+
+    int q_row = -1;
+    bf16x8 a[4];
+    f32x4 wv[4];
+    u32x4 cur[8];
+    bool ok = fetch(b, j, cur);
+    for (uint32_t it = s; it < pe; ++it) {
+      // prefetch the next page of the range while this one is computed
+      int nb = b;
+      uint32_t nj = j;
+      u32x4 nxt[8];
+      bool nok = false;
+      if (it + 1 < pe) {
+        window_find(W, it + 1, sh, false, nb, nj);
+        nok = fetch(nb, nj, nxt);
+      }
+      if (b != q_row) {
+        // query operand A (32 heads x 16 dims per step): lane holds head n,
+        // dims 16*kb + 8*half .. +7 = chunk 2*kb + half of that head's row
+        const rsrc_t qr = make_rsrc(q + (int64_t)b * (kHeads * kDim), kHeads * kRowBytes);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          a[kb] = __builtin_bit_cast(bf16x8,
+                                     __builtin_amdgcn_raw_buffer_load_b128(qr, n * kRowBytes + (2 * kb + half) * 16, 0, 0));
+        // head weights in accumulator order: register r of a lane holds head
+        // 8*(r/4) + 4*half + r%4, so group g = r/4 is the float4 at head 8*g + 4*half
+        const rsrc_t wr = make_rsrc(w + (int64_t)b * kHeads, kHeads * sizeof(float));
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          wv[g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, (8 * g + 4 * half) * 4, 0, 0));
+        q_row = b;
+      }
+      const int len = clamp_len(seq_lens[b], sh.width);
+      const int base = (int)j * kPage;
+      float val = __builtin_nanf("");  // a page id outside the pool scores NaN
+      if (ok) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) tile[lds_slot(i * 8 + (lane >> 3), lane & 7)] = cur[i];
+        __syncthreads();
+        // keys operand B (16 dims x 32 positions per step): lane holds position
+        // n of the half page, dims 16*kb + 8*half .. +7
+        f32x16 acc0 = {};  // positions 0..31 of the page
+        f32x16 acc1 = {};  // positions 32..63
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const int col = 2 * kb + half;
+          const bf16x8 b0 = __builtin_bit_cast(bf16x8, tile[lds_slot(n, col)]);
+          const bf16x8 b1 = __builtin_bit_cast(bf16x8, tile[lds_slot(n + 32, col)]);
+          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b0, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b1, acc1, 0, 0, 0);
+        }
+        __syncthreads();  // the tile is rewritten for the next page
+        // weighted ReLU over this lane's 16 heads, then the other 16 from lane ^ 32
+        float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            p0 = __builtin_fmaf(wv[g][r], __builtin_fmaxf(acc0[4 * g + r], 0.f), p0);
+            p1 = __builtin_fmaf(wv[g][r], __builtin_fmaxf(acc1[4 * g + r], 0.f), p1);
+          }
+        }
+        p0 += __shfl_xor(p0, 32);
+        p1 += __shfl_xor(p1, 32);
+        // lane < 32 owns position lane of the first half, lane >= 32 position lane of the second
+        val = half ? p1 : p0;
+      }
+      if (base + lane >= len) val = -__builtin_inff();  // partial last page
+      const rsrc_t out = make_rsrc(logits + (int64_t)b * sh.width + base, kPage * sizeof(float));
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), out, lane * 4, 0, 0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
+      ok = nok;
+      b = nb;
+      j = nj;
+    }
+  }
+
+  if (e > n_pages) {
+    // -inf tail chunks
+    Window W{0, 0, 0, 0, 0};
+    window_load(W, sh, true);
+    const u32x4 ninf = {0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u};
+    for (uint32_t it = max(s, n_pages); it < e; ++it) {
+      int b;
+      uint32_t c;
+      window_find(W, it - n_pages, sh, true, b, c);
+      const RowWork r = row_work(sh, b);
+      const uint32_t c0 = r.tail0 + c * kTailChunk, c1 = min(r.tail1, c0 + kTailChunk);
+      const rsrc_t row = make_rsrc(logits + (int64_t)b * sh.width, (uint32_t)sh.width * 4u);
+      // c0 and c1 are multiples of 4 (page and row boundaries): whole 16-byte stores
+      for (uint32_t p = c0 + 4 * lane; p < c1; p += 256) __builtin_amdgcn_raw_buffer_store_b128(ninf, row, p * 4, 0, 0);
+    }
+  }
 }
 
 __global__ __launch_bounds__(256) void hwm_kernel(const int32_t* __restrict__ seq_lens, int32_t batch,
@@ -139,14 +277,36 @@ __global__ __launch_bounds__(256) void hwm_kernel(const int32_t* __restrict__ se
   }
 }
 
+// Compute units of the device `stream` runs on (queried once per device).
+int cu_count(hipStream_t stream) {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (stream == nullptr || hipStreamGetDevice(stream, &dev) != hipSuccess) {
+    if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  }
+  if (dev < 0 || dev >= 64) dev = 0;
+  if (cached[dev] == 0) {
+    int count = 0;
+    if (hipDeviceGetAttribute(&count, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || count <= 0)
+      count = 256;
+    cached[dev] = count;
+  }
+  return cached[dev];
+}
+
 }  // namespace
 
 hipError_t launch_score(const void* q, const float* w, const void* k_pool, int64_t num_pages,
                         const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
                         int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream) {
-  hipLaunchKernelGGL(score_kernel, dim3(max_pages, batch), dim3(64), 0, stream,
-                     static_cast<const uint16_t*>(q), w, static_cast<const uint16_t*>(k_pool), num_pages,
-                     page_table, seq_lens, max_pages, logits, row_hwm);
+  // as many one-wave workgroups as stay resident, but no more than the largest
+  // list these shapes allow (every slot a page, plus every tail chunk)
+  const int64_t width = (int64_t)max_pages * kPage;
+  const int64_t most = (int64_t)batch * max_pages + (int64_t)batch * ((width + kTailChunk - 1) / kTailChunk);
+  const int grid = (int)std::min<int64_t>((int64_t)cu_count(stream) * kWavesPerCU, most);
+  hipLaunchKernelGGL(score_kernel, dim3(grid), dim3(64), 0, stream, static_cast<const uint16_t*>(q), w,
+                     static_cast<const uint16_t*>(k_pool), num_pages, page_table, seq_lens, batch, max_pages,
+                     logits, row_hwm);
   if (row_hwm != nullptr) {
     // after every workgroup of the score kernel has read the old marks
     hipLaunchKernelGGL(hwm_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, seq_lens, batch,

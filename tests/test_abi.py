@@ -58,7 +58,7 @@ def test_score_null(lib, field):
 
 
 @pytest.mark.parametrize("over", [dict(batch=0), dict(batch=-1), dict(batch=65536), dict(max_pages=0),
-                                  dict(max_pages=(1 << 22) + 1), dict(num_pages=0), dict(num_pages=-3)])
+                                  dict(max_pages=(1 << 22) + 1), dict(batch=64, max_pages=(1 << 20) + 1), dict(num_pages=0), dict(num_pages=-3)])
 def test_score_shape(lib, over):
     assert lib.dsa_indexer_score(*score_args(**over)) == SHAPE
 
