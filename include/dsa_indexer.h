@@ -107,8 +107,10 @@ int dsa_indexer_score(const void *q, const float *w, const void *k_pool, int64_t
                       const int32_t *page_table, const int32_t *seq_lens, int32_t batch,
                       int32_t max_pages, float *logits, int32_t *row_hwm, hipStream_t stream);
 
-/* Bytes of device workspace dsa_indexer_topk needs for these sizes
- * (0 means the workspace pointer may be NULL). */
+/* Bytes of device workspace dsa_indexer_topk needs for these sizes: 0 when
+ * max_c4 <= 4096 (the workspace may then be NULL) or the sizes are out of
+ * range, else batch * ceil(max_c4 / 4096) * (8 + 32768) bytes, about twice the
+ * logits' own size. */
 size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k);
 
 /*
@@ -127,9 +129,20 @@ size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k
  *   out_idx    int32 [batch][k]: the chosen positions in ascending order,
  *              then -1 in the remaining k - min(k, L) slots
  *   out_vals   NULL, or fp32 [batch][k]: logits at out_idx, NaN in padding
- *   workspace  device buffer of ws_bytes >= dsa_indexer_topk_workspace_bytes()
- *              (may be NULL when that is 0)
+ *   workspace  device buffer, 16-byte aligned, of ws_bytes >=
+ *              dsa_indexer_topk_workspace_bytes() (may be NULL when that is
+ *              0); its contents on entry do not matter and are overwritten.
+ *              Calls that may overlap (other streams) need workspaces of
+ *              their own
  *   stream     HIP stream to enqueue on
+ *
+ * Two kernels are enqueued. For rows longer than 4096 positions, a segment
+ * kernel splits the row into segments of 4096 positions, one workgroup each,
+ * and writes each segment's likely members of the top k (keys at or above a
+ * sampled cut, with their positions) to the workspace; a row kernel then
+ * selects the top k of each row from those candidates, and falls back to a
+ * select over the whole row whenever the candidates cannot be shown to hold
+ * the whole top k. The result never depends on the sampling.
  */
 int dsa_indexer_topk(const float *logits, const int32_t *seq_lens, int32_t batch, int32_t max_c4,
                      int32_t k, int32_t *out_idx, float *out_vals, void *workspace,

@@ -125,6 +125,19 @@ def topk_workspace_bytes(batch: int, max_c4: int, k: int) -> int:
     return int(load().dsa_indexer_topk_workspace_bytes(batch, max_c4, k))
 
 
+def topk_workspace(batch: int, max_c4: int, k: int, device="cuda"):
+    """A top-k workspace for these sizes (a uint8 tensor; None if none is needed)."""
+    import torch
+
+    need = topk_workspace_bytes(batch, max_c4, k)
+    if need == 0:
+        return None
+    return torch.empty(need, dtype=torch.uint8, device=device)
+
+
+_workspaces = {}  # (device, bytes) -> workspace reused by topk() calls that pass none
+
+
 def topk(logits, seq_lens, k, out_idx=None, out_vals=None, with_values=False, workspace=None,
          stream=None):
     """Top-k positions [B, k] (int32, ascending, -1 padded) of each row, and
@@ -143,8 +156,13 @@ def topk(logits, seq_lens, k, out_idx=None, out_vals=None, with_values=False, wo
     if out_vals is not None:
         _check(out_vals, "out_vals", (torch.float32,), (B, k), dev)
     need = topk_workspace_bytes(B, N, k)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    if workspace is None:
+        # one cached workspace per device and size: calls in stream order can share
+        # it (overlapping calls on other streams need their own)
+        key = (str(dev), need)
+        if key not in _workspaces:
+            _workspaces[key] = topk_workspace(B, N, k, device=dev)
+        workspace = _workspaces[key]
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     st = load().dsa_indexer_topk(

@@ -57,10 +57,9 @@ int dsa_indexer_score(const void* q, const float* w, const void* k_pool, int64_t
 }
 
 size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k) {
-  (void)batch;
-  (void)max_c4;
   (void)k;
-  return 0;
+  if (batch < 1 || batch > kMaxBatch || max_c4 < 1 || max_c4 > dsa::kMaxRowPositions) return 0;
+  return dsa::topk_workspace_words(batch, max_c4) * sizeof(uint32_t);
 }
 
 int dsa_indexer_topk(const float* logits, const int32_t* seq_lens, int32_t batch, int32_t max_c4,
@@ -71,9 +70,10 @@ int dsa_indexer_topk(const float* logits, const int32_t* seq_lens, int32_t batch
   if (k < 1 || k > max_c4) return DSA_ERR_K;
   const size_t need = dsa_indexer_topk_workspace_bytes(batch, max_c4, k);
   if (ws_bytes < need || (need > 0 && workspace == nullptr)) return DSA_ERR_WORKSPACE;
-  if (misaligned4(logits) || misaligned4(seq_lens) || misaligned4(out_idx) || misaligned4(out_vals))
+  if (misaligned4(logits) || misaligned4(seq_lens) || misaligned4(out_idx) || misaligned4(out_vals) ||
+      misaligned16(workspace))
     return DSA_ERR_ALIGN;
-  return from_hip(dsa::launch_topk(logits, seq_lens, batch, max_c4, k, out_idx, out_vals, stream));
+  return from_hip(dsa::launch_topk(logits, seq_lens, batch, max_c4, k, out_idx, out_vals, workspace, stream));
 }
 
 }  // extern "C"

@@ -40,8 +40,11 @@ hipError_t launch_score(const void* q, const float* w, const void* k_pool, int64
                         const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
                         int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream);
 
-// Enqueue the top-k kernel.
+// 32-bit words of top-k workspace for these sizes.
+size_t topk_workspace_words(int32_t batch, int32_t max_c4);
+
+// Enqueue the top-k kernels (workspace: topk_workspace_words words, any contents).
 hipError_t launch_topk(const float* logits, const int32_t* seq_lens, int32_t batch, int32_t max_c4,
-                       int32_t k, int32_t* out_idx, float* out_vals, hipStream_t stream);
+                       int32_t k, int32_t* out_idx, float* out_vals, void* workspace, hipStream_t stream);
 
 }  // namespace dsa

@@ -1,4 +1,4 @@
-// Top-k kernel of the DSA indexer decode step on gfx950.
+// Top-k of the DSA indexer decode step on gfx950.
 //
 // What it computes (page "The O(Actual) Indexer", section "The Benchmark
 // Results": the top-k that consumes the indexer's full-width logits): for each
@@ -8,54 +8,69 @@
 // describe, it never touches positions at or past L, so its cost follows the
 // actual length too.
 //
-// One 1024-lane workgroup per request works on order-preserving 32-bit keys
-// (larger float <=> larger key). Lane t holds the 32 consecutive positions
-// [32 t, 32 t + 32) of a block of kBlock = 32768 positions in registers, read
-// with eight 16-byte loads that are all in flight together.
+// Keys. Scores become order-preserving 32-bit keys (larger float <=> larger
+// key; -0 and +0 equal; NaN below -inf). The k-th largest key T is found by an
+// exact MSB-first radix select with digits of 11, 11 and 10 bits; r is the
+// number of keys == T that belong to the top k (the lowest positions first).
+// Before any point in position order, (keys > T before it) + min(r, keys == T
+// before it) positions are taken, so counting those two kinds of keys in
+// position order places every chosen position.
 //
-// Candidate path (a row of one block): a row of at most kCap positions is its
-// own candidate set; a longer row counts one sampled key per lane into a
-// 2048-bin histogram of the top 11 key bits, and the lower edge of the bin
-// holding a generous estimate of the k-th largest sample becomes a cut. The
-// keys >= cut are counted exactly; if there are at least k (so every key of
-// the top k is among them) and at most kCap, each lane writes its candidates
-// (key, position) to LDS at an offset from one block-wide scan, which keeps
-// them in position order. An exact MSB-first radix select with digits of 11,
-// 11 and 10 bits over the candidates gives the k-th largest key T and r, the
-// number of keys == T in the top k: each pass counts the candidates matching
-// the digits fixed so far into a 2048-bin LDS histogram, and a block-wide scan
-// over the bins, two per lane from the top bin down, finds the bin holding the
-// k-th largest.
+// Two kernels, so that no workgroup ever waits on another one:
+//  * Segment kernel (rows longer than kSeg positions only; grid: segments x
+//    requests, 256 lanes). A row is cut into segments of kSeg positions, so a
+//    long row is read by many compute units at once; lane t of a segment's
+//    workgroup holds the 16 consecutive positions at 16 t in registers. Two
+//    sampled keys per lane are counted into a histogram of the first digit,
+//    and the lower edge of the bin holding a generous estimate of the
+//    segment's share of the top k becomes its cut. Each wave writes its keys
+//    >= cut with their positions, in position order, to its own sub-slot of
+//    the workspace (so no scan spans the workgroup), and records its count.
+//  * Row kernel (one 1024-lane workgroup per request, so that many loads are
+//    in flight for the one compute unit). A row of at most kSeg positions is
+//    its own candidate set, read straight from the logits. A longer row
+//    gathers the sub-slots into LDS in order, hence position order: the first
+//    kSpec pairs of the first kSpecSlots sub-slots are loaded with 16-byte
+//    loads together with the counts, before the counts are known. An exact
+//    radix select over the candidates gives T; if T is at or above every
+//    segment's cut, each key a segment left out is below T, so the candidates
+//    hold the whole top k and the chosen positions are written from them.
+//    Otherwise (a cut above T, fewer than k or more than kCap candidates) the
+//    workgroup selects over the whole row instead, re-reading it from memory.
 //
-// Full path (a longer row, or a cut that missed): the same radix select over
-// every key, re-reading the row block by block, out of line so that its
-// registers are allocated apart from the candidate path's.
-//
-// Both paths place the chosen positions with one scan: before any point in
-// position order, (keys > T before it) + min(r, keys == T before it) positions
-// are taken, so a scan of the two counts packed in one word gives every lane
-// its output offset. Values are rebuilt from the keys (-0 is reported as +0,
-// any NaN as one NaN pattern). Wave-level scans use DPP row shifts and row
-// broadcasts.
+// A radix pass counts into a histogram in LDS; one wave then reads the whole
+// histogram and finds the digit (in the segment kernel every wave does so
+// itself, which spares a broadcast).
 #include "common.h"
 
 namespace dsa {
 namespace {
 
-constexpr int kThreads = 1024;
-constexpr int kWaves = kThreads / 64;
-constexpr int kBins = 2048;                      // 11-bit digits
-constexpr int kHistWords = kBins + kBins / 32;   // one pad word per 32 bins
-constexpr int kPerLane = 32;                     // consecutive positions per lane
-constexpr int kBlock = kPerLane * kThreads;      // 32768 positions per block
-constexpr int kCap = 8192;                       // candidates held in LDS
-constexpr uint32_t kNoPick = 0xFFFFFFFFu;
+constexpr int kBins = 2048;  // 11-bit digits (the last digit has 10 bits)
+
+constexpr int kSegThreads = 256;              // segment kernel
+constexpr int kSegWaves = kSegThreads / 64;
+constexpr int kSeg = 4096;                    // positions per segment workgroup
+constexpr int kPerLane = kSeg / kSegThreads;  // 16 consecutive positions per lane
+constexpr int kSub = kSeg / kSegWaves;        // 1024 positions per wave: one sub-slot
+constexpr int kRecWords = 8;                  // per segment: kept count of each wave, cut key, unused
+
+constexpr int kRowThreads = 1024;             // row kernel
+constexpr int kRowWaves = kRowThreads / 64;
+constexpr int kCap = 16384;                   // candidates a row workgroup holds in LDS
+constexpr int kRound = 256;                   // sub-slot records per gather round
+constexpr int kSpecSlots = 32;                // sub-slots read before their counts are known
+constexpr int kSpec = 256;                    // pairs read ahead per such sub-slot
+constexpr int kSweep = 16 * kRowThreads;      // positions per block of the whole-row output sweep
+
+static_assert(kSegWaves * 64 == kSegThreads && kPerLane * kSegThreads == kSeg, "segment work split");
+static_assert(2 * kRowThreads * 4 == kSpecSlots * kSpec, "read-ahead: four 16-byte loads per lane");
 
 // Monotone map float -> uint32: a > b as floats (with -0 == +0) iff key(a) >
 // key(b). Non-negative floats get the sign bit set, negative ones are
 // complemented; NaN maps to 1, below the key of every number (-inf maps to
-// 0x007FFFFF). Key 0 marks an unused slot past the row's length, so a key is
-// valid iff it is >= 1.
+// 0x007FFFFF). Key 0 marks a slot past the row's length, so a key is valid iff
+// it is >= 1.
 __device__ __forceinline__ uint32_t order_key(float x) {
   const uint32_t u = __float_as_uint(x + 0.0f);  // -0 + 0 = +0
   const uint32_t key = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
@@ -66,18 +81,29 @@ __device__ __forceinline__ uint32_t key_to_bits(uint32_t key) {
   return (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
 }
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
 __device__ __forceinline__ uint32_t load_b32(rsrc_t r, int i) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, i * 4, 0, 0);
 }
 __device__ __forceinline__ void store_b32(rsrc_t r, int i, uint32_t v) {
   __builtin_amdgcn_raw_buffer_store_b32(v, r, i * 4, 0, 0);
 }
+// Pair i (words 2i, 2i + 1) of a buffer of pairs.
+__device__ __forceinline__ u32x2 load_pair(rsrc_t r, int i) {
+  return __builtin_amdgcn_raw_buffer_load_b64(r, i * 8, 0, 0);
+}
+__device__ __forceinline__ void store_pair(rsrc_t r, int i, uint32_t a, uint32_t b) {
+  u32x2 v;
+  v.x = a;
+  v.y = b;
+  __builtin_amdgcn_raw_buffer_store_b64(v, r, i * 8, 0, 0);
+}
 
-// Digit of a key in pass p (0, 1, 2): bits 31..21, 20..10, 9..0.
-__device__ __forceinline__ int digit_shift(int pass) { return pass == 0 ? 21 : (pass == 1 ? 10 : 0); }
-__device__ __forceinline__ uint32_t digit_mask(int pass) { return pass == 2 ? 0x3FFu : 0x7FFu; }
-// LDS word of histogram bin b (a pad word after every 32 bins).
-__device__ __forceinline__ int hist_word(uint32_t b) { return (int)(b + (b >> 5)); }
+// LDS word of histogram bin b. Within each group of 32 bins the eight 4-bin
+// chunks are permuted by the group index, so that the lanes of a wave, each
+// reading its own group chunk by chunk, spread over the LDS banks.
+__device__ __forceinline__ uint32_t hslot(uint32_t b) { return b ^ (((b >> 5) & 7u) << 2); }
 
 // Inclusive scan over the 64 lanes of a wave: row shifts by 1, 2, 4, 8 scan
 // each row of 16 lanes, then row broadcasts of lanes 15 and 31 carry the row
@@ -92,81 +118,144 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
   return v;
 }
 
-// Inclusive scan of v over the block's lanes in lane order, and the block
-// total; `part` is kWaves words of LDS scratch (16-byte aligned). Every lane
-// of the block must call it.
-__device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t* part, uint32_t* total) {
+// Lanes of this wave below the calling one whose bit is set in mask.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// Inclusive scans of a and b over the workgroup's lanes in lane order, and
+// their totals; `part` is 2 * kWaves words of LDS. Every lane must call it;
+// it ends with a barrier, after which part may be rewritten.
+template <int kWaves>
+__device__ __forceinline__ void block_scan2(uint32_t& a, uint32_t& b, uint32_t* part, uint32_t* tot_a, uint32_t* tot_b) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  v = wave_inclusive_scan(v);
-  if (lane == 63) part[wave] = v;
+  a = wave_inclusive_scan(a);
+  b = wave_inclusive_scan(b);
+  if (lane == 63) {
+    part[wave] = a;
+    part[kWaves + wave] = b;
+  }
   __syncthreads();
-  const u32x4* p4 = reinterpret_cast<const u32x4*>(part);
-  uint32_t add = 0, all = 0;
+  uint32_t add_a = 0, add_b = 0, all_a = 0, all_b = 0;
 #pragma unroll
-  for (int q = 0; q < kWaves / 4; ++q) {
-    const u32x4 w4 = p4[q];
+  for (int wv = 0; wv < kWaves; ++wv) {
+    const uint32_t pa = part[wv], pb = part[kWaves + wv];
+    add_a += wv < wave ? pa : 0u;
+    add_b += wv < wave ? pb : 0u;
+    all_a += pa;
+    all_b += pb;
+  }
+  __syncthreads();
+  a += add_a;
+  b += add_b;
+  *tot_a = all_a;
+  *tot_b = all_b;
+}
+
+// From a histogram of kNB bins in LDS (complete, after a barrier), the bin
+// holding the rank-th largest counted key (rank = rank_of(total counted) >=
+// 1) and the number of counted keys in higher bins; {0, total} if rank
+// exceeds the total. Called by whole waves; each wave reads every bin and
+// finds the answer itself (lane l owns the kNB / 64 bins just below the top
+// kNB / 64 * l), so no barrier or broadcast follows.
+struct Pick {
+  uint32_t bin, above;
+};
+template <int kNB, typename RankOf>
+__device__ __forceinline__ Pick wave_pick(const uint32_t* hist, RankOf rank_of) {
+  constexpr int kPer = kNB / 64;    // bins per lane
+  constexpr int kChunks = kPer / 4;
+  const int lane = threadIdx.x & 63;
+  const uint32_t lo = (uint32_t)(kNB - kPer * (lane + 1));  // the lane's lowest bin
+  uint32_t c[kPer];
+#pragma unroll
+  for (int q = 0; q < kChunks; ++q) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(hist + hslot(lo + 4 * q));  // bins lo + 4q .. + 3
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      add += (4 * q + e < wave) ? w4[e] : 0u;
-      all += w4[e];
+      const uint32_t x = v[e];
+      c[4 * q + e] = x;
     }
   }
-  __syncthreads();
-  *total = all;
-  return v + add;
-}
-
-// The bin holding the rank-th largest of the counted keys, rank =
-// rank_of(total counted): returns {bin, keys in higher bins, total}, or
-// {kNoPick, total, total} if rank exceeds the total.
-struct Pick {
-  uint32_t bin, above, total;
-};
-template <typename RankOf>
-__device__ __forceinline__ Pick pick_bin(const uint32_t* h, RankOf rank_of, uint32_t* part, uint32_t* pick) {
-  const int tid = threadIdx.x;
-  // lane t owns bins 2047-2t and 2046-2t, so a lane-order scan runs from the top bin down
-  const uint32_t hi = (uint32_t)(kBins - 1 - 2 * tid), lo = hi - 1;
-  const uint32_t h_hi = h[hist_word(hi)], h_lo = h[hist_word(lo)];
-  uint32_t total;
-  const uint32_t incl = block_inclusive_scan(h_hi + h_lo, part, &total);  // keys in bins >= lo
-  const uint32_t rank = rank_of(total);
-  const uint32_t above_hi = incl - h_lo - h_hi;                            // keys in bins > hi
-  if (above_hi < rank && above_hi + h_hi >= rank) {
-    pick[0] = hi;
-    pick[1] = above_hi;
-  } else if (above_hi + h_hi < rank && incl >= rank) {
-    pick[0] = lo;
-    pick[1] = above_hi + h_hi;
-  } else if (tid == 0 && rank > total) {
-    pick[0] = kNoPick;
-    pick[1] = total;
+  uint32_t cs[kChunks], s = 0;
+#pragma unroll
+  for (int q = 0; q < kChunks; ++q) {
+    cs[q] = c[4 * q] + c[4 * q + 1] + c[4 * q + 2] + c[4 * q + 3];
+    s += cs[q];
   }
-  __syncthreads();
-  Pick p{pick[0], pick[1], total};
-  __syncthreads();  // pick[] is rewritten by the next call
-  return p;
+  const uint32_t incl = wave_inclusive_scan(s);
+  const uint32_t total = __builtin_amdgcn_readlane(incl, 63);
+  const uint32_t rank = rank_of(total);
+  const uint32_t excl = incl - s;
+  const uint64_t hit = __ballot(excl < rank && rank <= incl);
+  if (hit == 0) return Pick{0u, total};
+  const int src = __builtin_ctzll(hit);
+  // in the lane holding it: the chunk, top chunk first, then the bin
+  uint32_t acc = excl, above_q = 0;
+  int qs = 0;
+  bool done = false;
+#pragma unroll
+  for (int q = kChunks - 1; q >= 0; --q) {
+    if (!done && acc + cs[q] >= rank) {
+      qs = q;
+      above_q = acc;
+      done = true;
+    }
+    acc += cs[q];
+  }
+  uint32_t e4[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int q = 0; q < kChunks; ++q) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) e4[e] = q == qs ? c[4 * q + e] : e4[e];
+  }
+  acc = above_q;
+  uint32_t bin = 0, above = 0;
+  done = false;
+#pragma unroll
+  for (int e = 3; e >= 0; --e) {
+    if (!done && acc + e4[e] >= rank) {
+      bin = lo + 4u * (uint32_t)qs + (uint32_t)e;
+      above = acc;
+      done = true;
+    }
+    acc += e4[e];
+  }
+  return Pick{(uint32_t)__builtin_amdgcn_readlane((int)bin, src), (uint32_t)__builtin_amdgcn_readlane((int)above, src)};
 }
 
-// LDS of the kernel, at namespace scope so the out-of-line full path reaches
-// it with LDS instructions too.
-__shared__ uint32_t hist[2][kHistWords];  // counted into alternately
-__shared__ uint32_t cand_key[kCap];
-__shared__ uint32_t cand_pos[kCap];
-__shared__ __attribute__((aligned(16))) uint32_t part[kWaves];
-__shared__ uint32_t pick[2];
+// Workspace layout (32-bit words), for B requests and n_seg segments per row:
+//   rec   [B][n_seg][kRecWords]           kept count of waves 0..3, cut key, unused
+//   pairs [B][n_seg][kSegWaves][kSub][2]  kept (key, position) of each wave, in position order
+__device__ __forceinline__ size_t ws_pairs(int b, int batch, int n_seg) {
+  return (size_t)batch * n_seg * kRecWords + (size_t)b * n_seg * 2 * kSeg;
+}
 
-// Keys of the block at `blk` into this lane's registers: key[j] is position
-// blk + 32 * lane + j; slots at or past len get key 0. With at least k valid
-// keys (the row is longer than k), the k-th largest key is a valid one, so a
-// key-0 slot never reaches a bin at or above it and is never taken.
-__device__ __forceinline__ void load_block(rsrc_t row, bool vec, int blk, int len, uint32_t (&key)[kPerLane]) {
-  const int base = blk + kPerLane * (int)threadIdx.x;
+// ---------------------------------------------------------------------------
+// Segment kernel
+// ---------------------------------------------------------------------------
+
+struct SegShared {
+  __attribute__((aligned(16))) uint32_t hist[kBins];
+};
+
+// One segment (seg) of request b's row of len positions (kSeg < len, k < len).
+__device__ __forceinline__ void process_segment(SegShared& sm, const float* __restrict__ logits, int b, int seg,
+                                                int len, int max_c4, int k, int n_seg, int batch,
+                                                uint32_t* __restrict__ ws) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int s0 = seg * kSeg;
+  const float* row_ptr = logits + (int64_t)b * max_c4;
+  // only positions [0, len) of the row are readable through this resource
+  const rsrc_t row = make_rsrc(row_ptr, (uint32_t)len * 4u);
+  const int base = s0 + kPerLane * tid;
   const int n = min(max(len - base, 0), kPerLane);
-  if (vec && n == kPerLane) {
+  uint32_t key[kPerLane];
+  if (n == kPerLane && (reinterpret_cast<uintptr_t>(row_ptr) & 15u) == 0) {
     u32x4 v[kPerLane / 4];
 #pragma unroll
-    for (int m = 0; m < kPerLane / 4; ++m) v[m] = __builtin_amdgcn_raw_buffer_load_b128(row, (base + 4 * m) * 4, 0, 0);
+    for (int m = 0; m < kPerLane / 4; ++m)
+      v[m] = __builtin_amdgcn_raw_buffer_load_b128(row, (base + 4 * m) * 4, 0, 0);
 #pragma unroll
     for (int m = 0; m < kPerLane / 4; ++m) {
 #pragma unroll
@@ -178,80 +267,362 @@ __device__ __forceinline__ void load_block(rsrc_t row, bool vec, int blk, int le
       }
     }
   } else {
+    // every load is issued (past len the resource reads 0), then masked
+    uint32_t bits[kPerLane];
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j)
-      key[j] = j < n ? order_key(__uint_as_float(load_b32(row, base + j))) : 0u;
+    for (int j = 0; j < kPerLane; ++j) bits[j] = load_b32(row, base + j);
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) key[j] = j < n ? order_key(__uint_as_float(bits[j])) : 0u;
+  }
+
+  // The segment's expected share of the top k is k * valid / len; keep at
+  // least 1.5 times that plus 32, judged from a 1-in-8 sample.
+  const int valid = min(len - s0, kSeg);
+  const float want = 1.5f * (float)k * ((float)valid / (float)len) + 32.0f;
+  const uint32_t share = want < (float)valid ? (uint32_t)want : (uint32_t)valid;
+  uint32_t cut = 1u;  // keep every valid key
+  if (share < (uint32_t)valid) {
+    for (int i = tid; i < kBins; i += kSegThreads) sm.hist[i] = 0u;
+    __syncthreads();
+    const int ja = tid & (kPerLane - 1), jb = (tid + kPerLane / 2) & (kPerLane - 1);
+    uint32_t ka = 0u, kb = 0u;  // key[ja], key[jb] without a lane-varying register index
+#pragma unroll
+    for (int j = 0; j < kPerLane; ++j) {
+      ka = j == ja ? key[j] : ka;
+      kb = j == jb ? key[j] : kb;
+    }
+    if (ka != 0u) atomicAdd(&sm.hist[hslot(ka >> 21)], 1u);
+    if (kb != 0u) atomicAdd(&sm.hist[hslot(kb >> 21)], 1u);
+    __syncthreads();
+    // aim 25% (+4 samples) above the share among the samples
+    const Pick p = wave_pick<kBins>(sm.hist, [&](uint32_t n_s) {
+      return (uint32_t)(1.25f * (float)share * ((float)n_s / (float)valid)) + 4u; });
+    cut = max(p.bin << 21, 1u);
+  }
+
+  // this wave's kept keys, in position order, into its sub-slot
+  uint32_t cm = 0u;  // this lane's kept keys, as a bit mask over its run
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) cm |= (key[j] >= cut ? 1u : 0u) << j;
+  const uint32_t mine = (uint32_t)__popc(cm);
+  const uint32_t incl = wave_inclusive_scan(mine);
+  uint32_t at = incl - mine;
+  uint32_t* pairs = ws + ws_pairs(b, batch, n_seg);
+  const rsrc_t slot = make_rsrc(pairs + ((size_t)seg * kSegWaves + wave) * 2 * kSub, kSub * 8u);
+#pragma unroll
+  for (int j = 0; j < kPerLane; ++j) {
+    if (cm & (1u << j)) {
+      store_pair(slot, (int)at, key[j], (uint32_t)(base + j));
+      ++at;
+    }
+  }
+  const rsrc_t rec = make_rsrc(ws + ((size_t)b * n_seg + seg) * kRecWords, kRecWords * 4u);
+  if (lane == 63) store_b32(rec, wave, incl);
+  if (tid == 0) store_b32(rec, kSegWaves, cut);
+}
+
+// Grid: requests x segment groups; workgroup (b, y) takes segments y, y +
+// gridDim.y, ... of request b's row. With the request index first, the
+// workgroups of one row share b's place in the round-robin order of
+// workgroups over the chip's XCDs when the batch is a multiple of 8, so they
+// run on the XCD (and L2) where the row kernel's workgroup b, which reads
+// their output, runs.
+__global__ __launch_bounds__(kSegThreads) void topk_segment_kernel(const float* __restrict__ logits,
+                                                                    const int32_t* __restrict__ seq_lens,
+                                                                    int32_t max_c4, int32_t k, int32_t n_seg,
+                                                                    uint32_t* __restrict__ ws) {
+  __shared__ SegShared sm;
+  const int b = blockIdx.x;
+  const int len = min(max(seq_lens[b], 0), max_c4);
+  if (len <= kSeg || len <= k) return;  // the row kernel handles such a row alone
+  for (int seg = blockIdx.y; seg * kSeg < len; seg += gridDim.y) {
+    process_segment(sm, logits, b, seg, len, max_c4, k, n_seg, (int)gridDim.x, ws);
+    __syncthreads();  // sm is reused by the next segment
   }
 }
 
-// Full path: exact radix select over every key of the row, re-reading the row
-// block by block in every sweep.
-__device__ __noinline__ void full_path(rsrc_t row, rsrc_t oi, rsrc_t ov, bool with_vals, bool vec, int len,
-                                       int k) {
-  const int tid = threadIdx.x;
-  uint32_t key[kPerLane];
-  for (int i = tid; i < 2 * kHistWords; i += kThreads) (&hist[0][0])[i] = 0u;
+// ---------------------------------------------------------------------------
+// Row kernel
+// ---------------------------------------------------------------------------
+
+// LDS of the row kernel, at namespace scope so the out-of-line whole-row path
+// reaches it with LDS instructions too.
+struct RowShared {
+  __attribute__((aligned(16))) uint32_t hist0[kBins];  // one histogram per radix pass
+  __attribute__((aligned(16))) uint32_t hist1[kBins];
+  __attribute__((aligned(16))) uint32_t hist2[kBins / 2];
+  uint32_t cand_key[kCap];
+  uint32_t cand_pos[kCap];
+  uint32_t cnt[kRound];   // per sub-slot of a gather round: kept count
+  uint32_t off[kRound];   //   its first candidate
+  uint32_t roff[kRound];  //   its first pair not read ahead, in the round's list of those
+  uint32_t part[2 * kRowWaves];
+  uint32_t bcast[2];
+  uint32_t max_cut;
+};
+__shared__ RowShared rs;
+
+__device__ __forceinline__ uint32_t* pass_hist(int pass) {
+  return pass == 0 ? rs.hist0 : (pass == 1 ? rs.hist1 : rs.hist2);
+}
+
+// Clears the three histograms and max_cut (a barrier must follow before
+// they are counted into).
+__device__ __forceinline__ void clear_hists() {
+  if (threadIdx.x == 0) rs.max_cut = 0u;
+  for (int i = threadIdx.x; i < kBins; i += kRowThreads) {
+    rs.hist0[i] = 0u;
+    rs.hist1[i] = 0u;
+    if (i < kBins / 2) rs.hist2[i] = 0u;
+  }
+}
+
+// Resolves one digit: counts the keys matching (T, mask) into pass's
+// histogram with `count`; wave 0 picks the digit of the k-th largest and
+// hands it to the others through LDS.
+template <int kPass, typename Count>
+__device__ __forceinline__ void radix_pass(uint32_t& T, uint32_t& mask, uint32_t& remaining, Count count) {
+  constexpr int shift = kPass == 0 ? 21 : (kPass == 1 ? 10 : 0);
+  constexpr uint32_t dmask = kPass == 2 ? 0x3FFu : 0x7FFu;
+  uint32_t* h = pass_hist(kPass);
+  count(h, shift, dmask);
   __syncthreads();
-  int cur = 0;
+  if ((threadIdx.x >> 6) == 0) {
+    const Pick p = wave_pick<(kPass == 2 ? kBins / 2 : kBins)>(h, [&](uint32_t) { return remaining; });
+    if (threadIdx.x == 0) {
+      rs.bcast[0] = p.bin;
+      rs.bcast[1] = p.above;
+    }
+  }
+  __syncthreads();
+  // (bcast is written again only after the next pass's first barrier)
+  T |= rs.bcast[0] << shift;
+  remaining -= rs.bcast[1];
+  mask |= dmask << shift;
+}
+
+// Exact radix select over the n candidates in LDS (n >= k): the k-th largest
+// key T and r, the number of keys == T taken. The histograms are clear on
+// entry.
+struct Kth {
+  uint32_t T, r;
+};
+__device__ __forceinline__ Kth select_candidates(int n, int k) {
+  const int tid = threadIdx.x;
   uint32_t T = 0u, mask = 0u, remaining = (uint32_t)k;
-  for (int pass = 0; pass < 3; ++pass) {
-    const int shift = digit_shift(pass);
-    const uint32_t dmask = digit_mask(pass);
-    for (int blk = 0; blk < len; blk += kBlock) {
-      load_block(row, vec, blk, len, key);
+  auto count = [&](uint32_t* h, int shift, uint32_t dmask) {
+    int i = tid;
+    for (; i + 3 * kRowThreads < n; i += 4 * kRowThreads) {
+      uint32_t kk[4];
 #pragma unroll
-      for (int j = 0; j < kPerLane; ++j) {
-        const uint32_t kk = key[j];
-        if ((kk & mask) == T) atomicAdd(&hist[cur][hist_word((kk >> shift) & dmask)], 1u);
+      for (int u = 0; u < 4; ++u) kk[u] = rs.cand_key[i + u * kRowThreads];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if ((kk[u] & mask) == T) atomicAdd(&h[hslot((kk[u] >> shift) & dmask)], 1u);
+    }
+    for (; i < n; i += kRowThreads) {
+      const uint32_t kk = rs.cand_key[i];
+      if ((kk & mask) == T) atomicAdd(&h[hslot((kk >> shift) & dmask)], 1u);
+    }
+  };
+  radix_pass<0>(T, mask, remaining, count);
+  radix_pass<1>(T, mask, remaining, count);
+  radix_pass<2>(T, mask, remaining, count);
+  return Kth{T, remaining};
+}
+
+// Writes the chosen positions from the n candidates in LDS (position order);
+// each lane takes a run of consecutive candidates.
+__device__ __forceinline__ void write_from_candidates(int n, Kth t, rsrc_t oi, rsrc_t ov, bool with_vals) {
+  const int tid = threadIdx.x;
+  const int per = (n + kRowThreads - 1) / kRowThreads;  // <= kCap / kRowThreads
+  const int c0 = min(tid * per, n), c1 = min(c0 + per, n);
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int i = c0; i < c1; ++i) {
+    const uint32_t kk = rs.cand_key[i];
+    n_gt += kk > t.T ? 1u : 0u;
+    n_eq += kk == t.T ? 1u : 0u;
+  }
+  const uint32_t my_gt = n_gt, my_eq = n_eq;
+  uint32_t tot_gt, tot_eq;
+  block_scan2<kRowWaves>(n_gt, n_eq, rs.part, &tot_gt, &tot_eq);
+  uint32_t eq_rank = n_eq - my_eq;
+  uint32_t pos = (n_gt - my_gt) + min(t.r, eq_rank);
+  for (int i = c0; i < c1; ++i) {
+    const uint32_t kk = rs.cand_key[i];
+    if (kk > t.T || (kk == t.T && eq_rank < t.r)) {
+      store_b32(oi, (int)pos, rs.cand_pos[i]);
+      if (with_vals) store_b32(ov, (int)pos, key_to_bits(kk));
+      ++pos;
+    }
+    eq_rank += kk == t.T ? 1u : 0u;
+  }
+}
+
+// Whole-row path: the same radix select over every key of the row, re-reading
+// it from memory in every sweep; out of line so that its registers are
+// allocated apart from the candidate path's. The histograms are clear on entry.
+__device__ __noinline__ void select_whole_row(rsrc_t row, int len, int k, rsrc_t oi, rsrc_t ov, bool with_vals) {
+  const int tid = threadIdx.x;
+  uint32_t T = 0u, mask = 0u, remaining = (uint32_t)k;
+  auto count = [&](uint32_t* h, int shift, uint32_t dmask) {
+    for (int i0 = 0; i0 < len; i0 += 8 * kRowThreads) {
+      uint32_t kk[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kk[u] = load_b32(row, i0 + u * kRowThreads + tid);  // 0 past len
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t x = i0 + u * kRowThreads + tid < len ? order_key(__uint_as_float(kk[u])) : 0u;
+        if (x != 0u && (x & mask) == T) atomicAdd(&h[hslot((x >> shift) & dmask)], 1u);
       }
     }
-    __syncthreads();
-    for (int i = tid; i < kHistWords; i += kThreads) hist[cur ^ 1][i] = 0u;
-    const Pick p = pick_bin(hist[cur], [&](uint32_t) { return remaining; }, part, pick);
-    cur ^= 1;
-    T |= p.bin << shift;
-    remaining -= p.above;
-    mask |= dmask << shift;
-  }
-  uint32_t gt_seen = 0, eq_seen = 0;  // block-uniform totals over earlier blocks
-  for (int blk = 0; blk < len; blk += kBlock) {
-    load_block(row, vec, blk, len, key);
+  };
+  radix_pass<0>(T, mask, remaining, count);
+  radix_pass<1>(T, mask, remaining, count);
+  radix_pass<2>(T, mask, remaining, count);
+  uint32_t gt_seen = 0, eq_seen = 0;  // workgroup-uniform totals of earlier blocks
+  for (int blk = 0; blk < len; blk += kSweep) {
+    const int base = blk + 16 * tid;
+    uint32_t key[16];
     uint32_t n_gt = 0, n_eq = 0;
 #pragma unroll
-    for (int j = 0; j < kPerLane; ++j) {
+    for (int j = 0; j < 16; ++j) key[j] = load_b32(row, base + j);  // 0 past len
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      key[j] = base + j < len ? order_key(__uint_as_float(key[j])) : 0u;
       n_gt += key[j] > T ? 1u : 0u;
       n_eq += key[j] == T ? 1u : 0u;
     }
-    const uint32_t packed = (n_gt << 16) | n_eq;  // block totals < 2^16: no carry
-    uint32_t blk_tot;
-    const uint32_t before = block_inclusive_scan(packed, part, &blk_tot) - packed;
-    uint32_t eq_rank = eq_seen + (before & 0xFFFFu);
-    uint32_t pos = gt_seen + (before >> 16) + min(remaining, eq_rank);
-    if (n_gt + n_eq != 0) {
-      const int base = blk + kPerLane * tid;
+    const uint32_t my_gt = n_gt, my_eq = n_eq;
+    uint32_t tot_gt, tot_eq;
+    block_scan2<kRowWaves>(n_gt, n_eq, rs.part, &tot_gt, &tot_eq);
+    uint32_t eq_rank = eq_seen + n_eq - my_eq;
+    uint32_t pos = gt_seen + (n_gt - my_gt) + min(remaining, eq_rank);
 #pragma unroll
-      for (int j = 0; j < kPerLane; ++j) {
-        const bool gt = key[j] > T, eq = key[j] == T;
-        if (gt || (eq && eq_rank < remaining)) {
-          store_b32(oi, (int)pos, (uint32_t)(base + j));
-          if (with_vals) store_b32(ov, (int)pos, key_to_bits(key[j]));
-          ++pos;
-        }
-        eq_rank += eq ? 1u : 0u;
+    for (int j = 0; j < 16; ++j) {
+      const bool gt = key[j] > T, eq = key[j] == T;
+      if (gt || (eq && eq_rank < remaining)) {
+        store_b32(oi, (int)pos, (uint32_t)(base + j));
+        if (with_vals) store_b32(ov, (int)pos, key_to_bits(key[j]));
+        ++pos;
       }
+      eq_rank += eq ? 1u : 0u;
     }
-    gt_seen += blk_tot >> 16;
-    eq_seen += blk_tot & 0xFFFFu;
+    gt_seen += tot_gt;
+    eq_seen += tot_eq;
   }
 }
 
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ logits,
-                                                         const int32_t* __restrict__ seq_lens,
-                                                         int32_t max_c4, int32_t k,
-                                                         int32_t* __restrict__ out_idx,
-                                                         float* __restrict__ out_vals) {
-  const int b = blockIdx.x;
+// Gathers the kept pairs of a row longer than kSeg into LDS, in sub-slot
+// order; returns the candidate count, or -1 if more than kCap. Raises
+// rs.max_cut (zero on entry) to the largest segment cut.
+__device__ __forceinline__ int gather_segments(const uint32_t* __restrict__ ws, int b, int batch, int n_seg, int len) {
   const int tid = threadIdx.x;
+  const int n_act = (len + kSeg - 1) / kSeg;
+  const int n_sub = n_act * kSegWaves;
+  const rsrc_t recs = make_rsrc(ws + (size_t)b * n_seg * kRecWords, (uint32_t)n_act * kRecWords * 4u);
+  const rsrc_t pairs = make_rsrc(ws + ws_pairs(b, batch, n_seg), (uint32_t)n_act * kSeg * 8u);
+  const int n_spec = min(kSpecSlots, n_sub);
+  int n = 0;
+  for (int c0 = 0; c0 < n_sub; c0 += kRound) {  // gather rounds of kRound sub-slots
+    const int u = c0 + tid;
+    const bool mine = tid < kRound && u < n_sub;
+    uint32_t cnt = 0u, cut = 0u;
+    if (mine) {
+      const int s = u / kSegWaves;
+      cnt = load_b32(recs, s * kRecWords + u % kSegWaves);
+      cut = (u % kSegWaves == 0) ? load_b32(recs, s * kRecWords + kSegWaves) : 0u;
+    }
+    // read ahead (first round): pairs 2q, 2q + 1 of the first kSpecSlots
+    // sub-slots' first kSpec pairs, q = tid + kRowThreads w
+    u32x4 spec[4];
+    if (c0 == 0) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int q = 2 * (tid + kRowThreads * w), v = q / kSpec, i = q % kSpec;
+        if (v < n_spec) spec[w] = __builtin_amdgcn_raw_buffer_load_b128(pairs, (v * kSub + i) * 8, 0, 0);
+      }
+    }
+    uint32_t m = cut;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    // pairs not read ahead
+    const uint32_t rest = (u < n_spec) ? (cnt > (uint32_t)kSpec ? cnt - kSpec : 0u) : cnt;
+    uint32_t incl = cnt, rincl = rest, tot, rtot;
+    block_scan2<kRowWaves>(incl, rincl, rs.part, &tot, &rtot);  // (its barriers also order max_cut's clearing)
+    if ((tid & 63) == 0) atomicMax(&rs.max_cut, m);
+    if ((uint32_t)n + tot > (uint32_t)kCap) return -1;  // workgroup-uniform
+    if (tid < kRound) {
+      rs.cnt[tid] = cnt;
+      rs.off[tid] = (uint32_t)n + incl - cnt;
+      rs.roff[tid] = rincl - rest;
+    }
+    __syncthreads();
+    if (c0 == 0) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const int q = 2 * (tid + kRowThreads * w), v = q / kSpec, i = q % kSpec;
+        if (v < n_spec) {
+          const uint32_t cv = rs.cnt[v], ov = rs.off[v];
+          if ((uint32_t)i < cv) {
+            rs.cand_key[ov + i] = spec[w][0];
+            rs.cand_pos[ov + i] = spec[w][1];
+          }
+          if ((uint32_t)i + 1 < cv) {
+            rs.cand_key[ov + i + 1] = spec[w][2];
+            rs.cand_pos[ov + i + 1] = spec[w][3];
+          }
+        }
+      }
+    }
+    // the rest, as one list over the round's sub-slots
+    const int m_sub = min(kRound, n_sub - c0);
+    constexpr int kUnroll = 4;
+    for (int j0 = 0; j0 < (int)rtot; j0 += kUnroll * kRowThreads) {
+      int src[kUnroll], dst[kUnroll];
+#pragma unroll
+      for (int w = 0; w < kUnroll; ++w) {
+        const int j = j0 + w * kRowThreads + tid;
+        src[w] = 0;
+        dst[w] = -1;
+        if (j < (int)rtot) {
+          // the sub-slot holding item j: the last one whose offset is <= j
+          int lo = 0, hi = m_sub;
+          while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (rs.roff[mid] <= (uint32_t)j) lo = mid;
+            else hi = mid;
+          }
+          const int skip = (c0 + lo < n_spec) ? kSpec : 0;
+          const int i = skip + (j - (int)rs.roff[lo]);  // pair index within the sub-slot
+          src[w] = (c0 + lo) * kSub + i;
+          dst[w] = (int)rs.off[lo] + i;
+        }
+      }
+      u32x2 c[kUnroll];
+#pragma unroll
+      for (int w = 0; w < kUnroll; ++w) c[w] = load_pair(pairs, src[w]);
+#pragma unroll
+      for (int w = 0; w < kUnroll; ++w) {
+        if (dst[w] >= 0) {
+          rs.cand_key[dst[w]] = c[w].x;
+          rs.cand_pos[dst[w]] = c[w].y;
+        }
+      }
+    }
+    n += (int)tot;
+    __syncthreads();  // cnt, off and roff are rewritten by the next round
+  }
+  return n;
+}
+
+__global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ logits,
+                                                                const int32_t* __restrict__ seq_lens,
+                                                                int32_t max_c4, int32_t k,
+                                                                int32_t* __restrict__ out_idx,
+                                                                float* __restrict__ out_vals,
+                                                                const uint32_t* __restrict__ ws, int32_t n_seg) {
+  const int b = blockIdx.x, tid = threadIdx.x;
   const int len = min(max(seq_lens[b], 0), max_c4);
   const float* row_ptr = logits + (int64_t)b * max_c4;
   // only positions [0, len) of the row are readable through this resource
@@ -263,110 +634,65 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 
   if (len <= k) {
     // every valid position is chosen
-    for (int i = tid; i < k; i += kThreads) {
+    for (int i = tid; i < k; i += kRowThreads) {
       store_b32(oi, i, i < len ? (uint32_t)i : 0xFFFFFFFFu);
       if (with_vals) store_b32(ov, i, i < len ? load_b32(row, i) : 0x7FC00000u);
     }
     return;
   }
-  const bool vec = (reinterpret_cast<uintptr_t>(row_ptr) & 15u) == 0;
 
-  if (len <= kBlock) {
-    uint32_t key[kPerLane];
-    load_block(row, vec, 0, len, key);
-    uint32_t cut = 1u;  // candidates: keys >= cut (1: every valid key)
-    bool ok = len <= kCap;
-    if (!ok && k <= kCap) {
-      for (int i = tid; i < kHistWords; i += kThreads) hist[0][i] = 0u;
-      __syncthreads();
-      // one sampled key per lane, spread over the lane's run
-      const int js = tid & (kPerLane - 1);
-      uint32_t ks = 0u;  // key[js] without a lane-varying register index
+  clear_hists();
+  int n;
+  if (len <= kSeg) {
+    // the row is its own candidate set
+    uint32_t bits[kSeg / kRowThreads];
 #pragma unroll
-      for (int j = 0; j < kPerLane; ++j) ks = j == js ? key[j] : ks;
-      if (ks != 0u) atomicAdd(&hist[0][hist_word(ks >> 21)], 1u);
-      __syncthreads();
-      // aim 25% (+16 samples) above the expected number of sampled keys in the top k
-      const Pick p = pick_bin(hist[0], [&](uint32_t n) {
-        return (uint32_t)(((uint64_t)k * n * 5u) / (4u * (uint64_t)len)) + 16u; }, part, pick);
-      ok = p.bin != kNoPick && p.bin != 0u;
-      cut = ok ? p.bin << 21 : 1u;
+    for (int m = 0; m < kSeg / kRowThreads; ++m) bits[m] = load_b32(row, m * kRowThreads + tid);  // 0 past len
+#pragma unroll
+    for (int m = 0; m < kSeg / kRowThreads; ++m) {
+      const int i = m * kRowThreads + tid;
+      if (i < len) {
+        rs.cand_key[i] = order_key(__uint_as_float(bits[m]));
+        rs.cand_pos[i] = (uint32_t)i;
+      }
     }
-    // candidates of this lane, as a bit mask over its run
-    uint32_t cm = 0u;
-#pragma unroll
-    for (int j = 0; j < kPerLane; ++j) cm |= (key[j] >= cut ? 1u : 0u) << j;
-    uint32_t n_cand;
-    const uint32_t mine = (uint32_t)__popc(cm);
-    uint32_t at = block_inclusive_scan(mine, part, &n_cand) - mine;
-    if (ok || n_cand <= (uint32_t)kCap) ok = n_cand >= (uint32_t)k && n_cand <= (uint32_t)kCap;
-    if (ok) {
-      const int base = kPerLane * tid;
-#pragma unroll
-      for (int j = 0; j < kPerLane; ++j) {
-        if (cm & (1u << j)) {
-          cand_key[at] = key[j];
-          cand_pos[at] = (uint32_t)(base + j);
-          ++at;
-        }
-      }
-      for (int i = tid; i < 2 * kHistWords; i += kThreads) (&hist[0][0])[i] = 0u;
-      __syncthreads();
-
-      // exact radix select over the candidates
-      int cur = 0;
-      uint32_t T = 0u, mask = 0u, remaining = (uint32_t)k;
-      for (int pass = 0; pass < 3; ++pass) {
-        const int shift = digit_shift(pass);
-        const uint32_t dmask = digit_mask(pass);
-        for (int i = tid; i < (int)n_cand; i += kThreads) {
-          const uint32_t kk = cand_key[i];
-          if ((kk & mask) == T) atomicAdd(&hist[cur][hist_word((kk >> shift) & dmask)], 1u);
-        }
-        __syncthreads();
-        for (int i = tid; i < kHistWords; i += kThreads) hist[cur ^ 1][i] = 0u;
-        const Pick p = pick_bin(hist[cur], [&](uint32_t) { return remaining; }, part, pick);
-        cur ^= 1;
-        T |= p.bin << shift;
-        remaining -= p.above;
-        mask |= dmask << shift;
-      }
-
-      // each lane takes a run of consecutive candidates
-      const int per = ((int)n_cand + kThreads - 1) / kThreads;  // <= kCap / kThreads
-      const int c0 = min(tid * per, (int)n_cand), c1 = min(c0 + per, (int)n_cand);
-      uint32_t n_gt = 0, n_eq = 0;
-      for (int i = c0; i < c1; ++i) {
-        const uint32_t kk = cand_key[i];
-        n_gt += kk > T ? 1u : 0u;
-        n_eq += kk == T ? 1u : 0u;
-      }
-      const uint32_t packed = (n_gt << 16) | n_eq;
-      uint32_t unused;
-      const uint32_t before = block_inclusive_scan(packed, part, &unused) - packed;
-      uint32_t eq_rank = before & 0xFFFFu;
-      uint32_t pos = (before >> 16) + min(remaining, eq_rank);
-      for (int i = c0; i < c1; ++i) {
-        const uint32_t kk = cand_key[i];
-        if (kk > T || (kk == T && eq_rank < remaining)) {
-          store_b32(oi, (int)pos, cand_pos[i]);
-          if (with_vals) store_b32(ov, (int)pos, key_to_bits(kk));
-          ++pos;
-        }
-        eq_rank += kk == T ? 1u : 0u;
-      }
+    n = len;
+  } else {
+    n = gather_segments(ws, b, (int)gridDim.x, n_seg, len);
+  }
+  __syncthreads();
+  if (n >= k) {  // n < 0: more than kCap candidates
+    const Kth t = select_candidates(n, k);
+    // every key a segment left out lies below its cut, hence below T
+    if (t.T >= rs.max_cut) {
+      write_from_candidates(n, t, oi, ov, with_vals);
       return;
     }
+    __syncthreads();  // every wave is done with the histograms
+    clear_hists();
+    __syncthreads();
   }
-  full_path(row, oi, ov, with_vals, vec, len, k);
+  select_whole_row(row, len, k, oi, ov, with_vals);
 }
 
 }  // namespace
 
+size_t topk_workspace_words(int32_t batch, int32_t max_c4) {
+  if (max_c4 <= kSeg) return 0;  // no row can need the segment kernel
+  const size_t n_seg = ((size_t)max_c4 + kSeg - 1) / kSeg;
+  return (size_t)batch * n_seg * (kRecWords + 2 * kSeg);  // records, then pairs
+}
+
 hipError_t launch_topk(const float* logits, const int32_t* seq_lens, int32_t batch, int32_t max_c4,
-                       int32_t k, int32_t* out_idx, float* out_vals, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_kernel, dim3(batch), dim3(kThreads), 0, stream, logits, seq_lens, max_c4, k,
-                     out_idx, out_vals);
+                       int32_t k, int32_t* out_idx, float* out_vals, void* workspace, hipStream_t stream) {
+  const int n_seg = (int)(((int64_t)max_c4 + kSeg - 1) / kSeg);
+  uint32_t* ws = static_cast<uint32_t*>(workspace);
+  // a row reaches the segment kernel only if it is longer than kSeg and than k
+  if (max_c4 > kSeg && k < max_c4)
+    hipLaunchKernelGGL(topk_segment_kernel, dim3(batch, min(n_seg, 65535)), dim3(kSegThreads), 0, stream, logits, seq_lens,
+                       max_c4, k, n_seg, ws);
+  hipLaunchKernelGGL(topk_row_kernel, dim3(batch), dim3(kRowThreads), 0, stream, logits, seq_lens, max_c4, k,
+                     out_idx, out_vals, ws, n_seg);
   return hipGetLastError();
 }
 

@@ -71,7 +71,7 @@ def test_score_alignment(lib, field, off):
 
 def topk_args(**over):
     args = dict(logits=A, seq_lens=A, batch=2, max_c4=128, k=16, out_idx=A, out_vals=None,
-                workspace=None, ws_bytes=0, stream=None)
+                workspace=A, ws_bytes=1 << 30, stream=None)
     args.update(over)
     return list(args.values())
 
@@ -91,6 +91,10 @@ def test_topk_rejects(lib, over, want):
 
 def test_topk_workspace_contract(lib):
     need = lib.dsa_indexer_topk_workspace_bytes(64, 32768, 2048)
-    assert need >= 0
-    if need > 0:
-        assert lib.dsa_indexer_topk(*topk_args(ws_bytes=need - 1, workspace=A, k=0)) in (K, WS)
+    assert need == 64 * 8 * (8 + 2 * 4096) * 4
+    assert lib.dsa_indexer_topk_workspace_bytes(64, 4096, 64) == 0  # one segment: no workspace
+    assert lib.dsa_indexer_topk_workspace_bytes(0, 32768, 2048) == 0
+    # every call below fails validation (nothing may reach a launch in these host-only tests)
+    assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=32768, k=2048, workspace=A, ws_bytes=need - 1)) == WS
+    assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=32768, k=2048, workspace=None, ws_bytes=need)) == WS
+    assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=32768, k=2048, workspace=A + 4, ws_bytes=need)) == ALIGN
