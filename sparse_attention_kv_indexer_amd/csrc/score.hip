@@ -20,9 +20,10 @@
 // pages past a length are never read (the early exit of the section "The
 // Benchmark Results"), and in the incremental mode the tail is not rewritten.
 // Each workgroup finds the requests its range starts in with wave scans over
-// windows of 64 request lengths, walks its range in order, loads q and w only
-// when the request changes, and prefetches the next page while it computes
-// the current one.
+// windows of 64 request lengths, walks its range in order, and loads q and w
+// only when the request changes. The walk is a three-stage pipeline: while a
+// page is computed, the next page's keys and the page id after it are in
+// flight.
 //
 // A page is read with eight fully coalesced 1 KiB wave loads, staged in LDS
 // under an XOR swizzle, and contracted against the request's 32 x 64 query
@@ -121,7 +122,7 @@ __device__ __forceinline__ void window_find(Window& W, uint32_t item, const Shap
   j = r - (uint32_t)__builtin_amdgcn_readlane((int)W.pre, l);
 }
 
-__global__ __launch_bounds__(64) void score_kernel(
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void score_kernel(
     const uint16_t* __restrict__ q,          // bf16 [B][32][64]
     const float* __restrict__ w,             // [B][32]
     const uint16_t* __restrict__ k_pool,     // bf16 [num_pages][64][64]
@@ -156,58 +157,68 @@ __global__ __launch_bounds__(64) void score_kernel(
     const uint32_t pe = min(e, n_pages);
     Window W{0, 0, 0, 0, 0};
     window_load(W, sh, false);
-    int b;
-    uint32_t j;
-    window_find(W, s, sh, false, b, j);
 
-    // key page of (request bb, slot jj) into dst; false if its id is outside the pool
-    auto fetch = [&](int bb, uint32_t jj, u32x4 (&dst)[8]) -> bool {
-      const int page = page_table[(int64_t)bb * max_pages + jj];
-      if (page < 0 || (int64_t)page >= num_pages) return false;  // never dereferenced
-      const rsrc_t kp = make_rsrc(k_pool + (int64_t)page * (kPage * kDim), kPageBytes);
+    // Three-stage pipeline over the range: while item `it` is computed, the
+    // key page of item it + 1 and the page id of item it + 2 are in flight.
+    // Page ids come in through vector loads, so that all three kinds of load
+    // complete in issue order and no wait for one stalls behind another; the
+    // loop is unrolled twice with ping-pong registers, so no register holding
+    // a pending load is ever copied (a copy would wait for the load). Every
+    // step issues the same loads whatever the data (an item past the range or
+    // an id outside the pool reads through an empty resource, which returns
+    // zeros without a memory access), so the compiler's in-order wait counts
+    // never fall back to waiting for everything in flight.
+    const rsrc_t none = make_rsrc(k_pool, 0u);
+    // page id load of item x (pending until key_load reads it); 0 past the range
+    auto id_load = [&](uint32_t x, int& bx, uint32_t& jx) -> uint32_t {
+      const bool in = x < pe;
+      if (in) window_find(W, x, sh, false, bx, jx);
+      const rsrc_t pt = in ? make_rsrc(page_table + (int64_t)bx * max_pages, (uint32_t)max_pages * 4u) : none;
+      return __builtin_amdgcn_raw_buffer_load_b32(pt, in ? (int)jx * 4 : 0, 0, 0);
+    };
+    // key page of a loaded id into dst; false if the id is outside the pool
+    // (then dst is zero and the page is never dereferenced)
+    auto key_load = [&](uint32_t id, u32x4 (&dst)[8]) -> bool {
+      const int page = __builtin_amdgcn_readfirstlane((int)id);
+      const bool ok = page >= 0 && (int64_t)page < num_pages;
+      const rsrc_t kp = ok ? make_rsrc(k_pool + (int64_t)page * (kPage * kDim), kPageBytes) : none;
       // 16-byte chunk c = 64 * i + lane is key row c / 8, column c % 8
 #pragma unroll
       for (int i = 0; i < 8; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b128(kp, (i * 64 + lane) * 16, 0, kNonTemporal);
-      return true;
+      return ok;
     };
 
     int q_row = -1;
     bf16x8 a[4];
     f32x4 wv[4];
-    u32x4 cur[8];
-    bool ok = fetch(b, j, cur);
-    for (uint32_t it = s; it < pe; ++it) {
-      // prefetch the next page of the range while this one is computed
-      int nb = b;
-      uint32_t nj = j;
-      u32x4 nxt[8];
-      bool nok = false;
-      if (it + 1 < pe) {
-        window_find(W, it + 1, sh, false, nb, nj);
-        nok = fetch(nb, nj, nxt);
-      }
-      if (b != q_row) {
+    // q and w of request bx, if not held already; called before the phase's
+    // other loads, so that waiting for them never waits for those
+    auto ensure_qw = [&](int bx) {
+      if (bx != q_row) {
         // query operand A (32 heads x 16 dims per step): lane holds head n,
         // dims 16*kb + 8*half .. +7 = chunk 2*kb + half of that head's row
-        const rsrc_t qr = make_rsrc(q + (int64_t)b * (kHeads * kDim), kHeads * kRowBytes);
+        const rsrc_t qr = make_rsrc(q + (int64_t)bx * (kHeads * kDim), kHeads * kRowBytes);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
           a[kb] = __builtin_bit_cast(bf16x8,
                                      __builtin_amdgcn_raw_buffer_load_b128(qr, n * kRowBytes + (2 * kb + half) * 16, 0, 0));
         // head weights in accumulator order: register r of a lane holds head
         // 8*(r/4) + 4*half + r%4, so group g = r/4 is the float4 at head 8*g + 4*half
-        const rsrc_t wr = make_rsrc(w + (int64_t)b * kHeads, kHeads * sizeof(float));
+        const rsrc_t wr = make_rsrc(w + (int64_t)bx * kHeads, kHeads * sizeof(float));
 #pragma unroll
         for (int g = 0; g < 4; ++g)
           wv[g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, (8 * g + 4 * half) * 4, 0, 0));
-        q_row = b;
+        q_row = bx;
       }
-      const int len = clamp_len(seq_lens[b], sh.width);
-      const int base = (int)j * kPage;
+    };
+    // scores of item (bx, jx) from its key page (q and w of bx held)
+    auto compute = [&](int bx, uint32_t jx, bool okx, const u32x4 (&page)[8]) {
+      const int len = clamp_len(seq_lens[bx], sh.width);
+      const int base = (int)jx * kPage;
       float val = __builtin_nanf("");  // a page id outside the pool scores NaN
-      if (ok) {
+      if (okx) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) tile[lds_slot(i * 8 + (lane >> 3), lane & 7)] = cur[i];
+        for (int i = 0; i < 8; ++i) tile[lds_slot(i * 8 + (lane >> 3), lane & 7)] = page[i];
         __syncthreads();
         // keys operand B (16 dims x 32 positions per step): lane holds position
         // n of the half page, dims 16*kb + 8*half .. +7
@@ -238,13 +249,37 @@ __global__ __launch_bounds__(64) void score_kernel(
         val = half ? p1 : p0;
       }
       if (base + lane >= len) val = -__builtin_inff();  // partial last page
-      const rsrc_t out = make_rsrc(logits + (int64_t)b * sh.width + base, kPage * sizeof(float));
+      const rsrc_t out = make_rsrc(logits + (int64_t)bx * sh.width + base, kPage * sizeof(float));
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), out, lane * 4, 0, 0);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) cur[i] = nxt[i];
-      ok = nok;
-      b = nb;
-      j = nj;
+    };
+
+    // state at the top of each half of the loop, for the item `it` it computes:
+    // its keys in KA (phase A) or KB (phase B), the id of it + 1 in flight
+    u32x4 KA[8], KB[8];
+    int bA = 0, bB = 0, bX = 0, bY = 0;
+    uint32_t jA = 0, jB = 0, jX = 0, jY = 0, PX = 0, PY = 0;
+    bool okA = false, okB = false;
+    uint32_t it = s;
+    const uint32_t PA = id_load(it, bA, jA);
+    PY = id_load(it + 1, bY, jY);
+    okA = key_load(PA, KA);
+    for (;;) {
+      // phase A: item it in KA; item it + 1's id in PY
+      ensure_qw(bA);
+      PX = id_load(it + 2, bX, jX);
+      okB = key_load(PY, KB);
+      bB = bY;
+      jB = jY;
+      compute(bA, jA, okA, KA);
+      if (++it >= pe) break;
+      // phase B: item it in KB; item it + 1's id in PX
+      ensure_qw(bB);
+      PY = id_load(it + 2, bY, jY);
+      okA = key_load(PX, KA);
+      bA = bX;
+      jA = jX;
+      compute(bB, jB, okB, KB);
+      if (++it >= pe) break;
     }
   }
 
