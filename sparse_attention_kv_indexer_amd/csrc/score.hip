@@ -296,7 +296,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void
       const uint32_t c0 = r.tail0 + c * kTailChunk, c1 = min(r.tail1, c0 + kTailChunk);
       const rsrc_t row = make_rsrc(logits + (int64_t)b * sh.width, (uint32_t)sh.width * 4u);
       // c0 and c1 are multiples of 4 (page and row boundaries): whole 16-byte stores
-      for (uint32_t p = c0 + 4 * lane; p < c1; p += 256) __builtin_amdgcn_raw_buffer_store_b128(ninf, row, p * 4, 0, 0);
+      // streaming stores: the tail is not read back soon (measured: faster where the tail dominates,
+      // unchanged elsewhere; the scored pages keep ordinary stores, which the top-k reads next)
+      for (uint32_t p = c0 + 4 * lane; p < c1; p += 256)
+        __builtin_amdgcn_raw_buffer_store_b128(ninf, row, p * 4, 0, kNonTemporal);
     }
   }
 }
