@@ -113,3 +113,18 @@ def test_sampled_cut_fallbacks(lib):
         xd, ld = _upload(x, lens)
         idx, vals = run_topk(lib, xd, ld, k)
         check_topk_exact(idx, vals, x, lens, k)
+
+
+def test_rows_with_many_segments(lib):
+    """A row long enough that the row kernel gathers its segments' candidates
+    in more than one round (more than 64 segments of 4096 positions), next to
+    a row that is its own candidate set and a row of exactly one segment."""
+    rng = np.random.default_rng(10)
+    B, N = 3, 300000
+    x = rng.standard_normal((B, N)).astype(np.float32)
+    lens = np.array([300000, 4096, 4097])
+    for k in (64, 2048):
+        say(f"topk many segments k={k}")
+        xd, ld = _upload(x, lens)
+        idx, vals = run_topk(lib, xd, ld, k)
+        check_topk_exact(idx, vals, x, lens, k)
