@@ -66,3 +66,33 @@ def test_nonnegative_weights(lib):
     assert np.all(got[fin] >= 0)
     ref, M, A = oracle_scores(inp)
     check_scores(got, ref, M, A)
+
+
+@pytest.mark.parametrize("seed", range(2))
+def test_large_batch_crosses_request_windows(lib, seed):
+    """More than 64 requests: the kernel maps work items to requests through
+    windows of 64 lengths, so a range of work can start in one window and end
+    in another. Rows of every kind are mixed in (empty, one partial page,
+    full), many of them a single page, and the stateless and incremental
+    tails must agree."""
+    import torch
+
+    rng = np.random.default_rng(200 + seed)
+    B, S = 300, 8
+    N = S * 64
+    lens = rng.integers(0, N, size=B, endpoint=True)
+    lens[rng.random(B) < 0.3] = 0
+    lens[rng.random(B) < 0.2] = 1
+    lens[::17] = N
+    inp = wl.random_case(300 + seed, B, S, lens=lens)
+    say(f"score large batch B={B} seed={seed}")
+    got, t, _ = run_score(lib, inp)
+    ref, M, A = oracle_scores(inp)
+    check_scores(got, ref, M, A)
+    # incremental mode from an all -inf row and zero marks, twice (second call: marks = lengths)
+    logits = torch.full((B, N), float("-inf"), device="cuda")
+    hwm = torch.zeros(B, dtype=torch.int32, device="cuda")
+    for rep in range(2):
+        lib.score(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"], out=logits, row_hwm=hwm)
+        torch.cuda.synchronize()
+        assert np.array_equal(logits.cpu().numpy().view(np.uint32), got.view(np.uint32)), rep

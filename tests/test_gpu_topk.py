@@ -128,3 +128,19 @@ def test_rows_with_many_segments(lib):
         xd, ld = _upload(x, lens)
         idx, vals = run_topk(lib, xd, ld, k)
         check_topk_exact(idx, vals, x, lens, k)
+
+
+def test_large_batch(lib):
+    """More than 64 requests with mixed lengths: rows of one segment, of many
+    segments, shorter than k, and empty."""
+    rng = np.random.default_rng(11)
+    B, N, k = 200, 20000, 300
+    x = rng.standard_normal((B, N)).astype(np.float32)
+    lens = rng.integers(0, N, size=B, endpoint=True)
+    lens[::7] = 0
+    lens[::11] = k - 1
+    lens[::13] = N
+    say(f"topk large batch B={B}")
+    xd, ld = _upload(x, lens)
+    idx, vals = run_topk(lib, xd, ld, k)
+    check_topk_exact(idx, vals, x, lens, k)
