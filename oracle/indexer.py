@@ -23,6 +23,11 @@ What it computes, and where the pages state it:
   length is -inf, and the output always has the full row width.
 * Top-k (section "The Benchmark Results": the downstream top-k over the
   logits): the k largest scores of positions [0, L) per request.
+* fp8 keys (an input format the pages only allude to: page "The Indexer
+  O(max_context) Breakthrough" mentions an fp8 KV cache, without saying how
+  the indexer's keys are stored): OCP FP8 E4M3 codes with one float32 scale
+  per key; the key is scale * decode(code), and the score is the same
+  formula on that key.
 
 Readings taken where the pages are silent (each is listed in the design
 notes): lengths are clamped to [0, row width]; a page id outside the pool in a
@@ -48,19 +53,41 @@ def bf16_bits_to_f64(bits: np.ndarray) -> np.ndarray:
     return u32.view(np.float32).astype(np.float64)
 
 
+def e4m3_to_f64(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 (e4m3fn) codes -> float64, exactly. Sign s, exponent field
+    e (bias 7), mantissa m: (-1)^s (m / 8) 2^-6 when e = 0, else
+    (-1)^s (1 + m / 8) 2^(e - 7); e = 15 with m = 7 is NaN (no infinities)."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    s, e, m = c >> 7, (c >> 3) & 15, c & 7
+    mag = np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * np.exp2(e - 7.0))
+    val = np.where(s == 1, -mag, mag)
+    return np.where((e == 15) & (m == 7), np.nan, val)
+
+
+def bf16_pages(k_bits):
+    """Page decoder of a bfloat16 key pool: page ids -> float64 [n, 64, D]."""
+    return lambda pages: bf16_bits_to_f64(k_bits[pages])
+
+
+def fp8_pages(k8, k_scale):
+    """Page decoder of an e4m3fn key pool with one scale per key."""
+    scale = np.asarray(k_scale, dtype=np.float64)
+    return lambda pages: e4m3_to_f64(k8[pages]) * scale[pages][..., None]
+
+
 def clamp_len(length: int, row_width: int) -> int:
     return int(min(max(int(length), 0), row_width))
 
 
-def gather_keys(k_bits: np.ndarray, table_row: np.ndarray, length: int):
-    """Keys of positions [0, length) of one request, as float64 [length, D],
-    and a boolean [length] flag of positions whose page id is outside the pool."""
-    num_pages = k_bits.shape[0]
+def gather_keys(decode, num_pages: int, table_row: np.ndarray, length: int):
+    """Keys of positions [0, length) of one request, as float64 [length, D]
+    (``decode`` maps page ids to their keys), and a boolean [length] flag of
+    positions whose page id is outside the pool."""
     n_slots = (length + PAGE - 1) // PAGE
     pages = np.asarray(table_row[:n_slots], dtype=np.int64)
     bad_page = (pages < 0) | (pages >= num_pages)
     safe = np.where(bad_page, 0, pages)
-    keys = bf16_bits_to_f64(k_bits[safe]).reshape(n_slots * PAGE, -1)[:length]
+    keys = decode(safe).reshape(n_slots * PAGE, -1)[:length]
     bad = np.repeat(bad_page, PAGE)[:length]
     return keys, bad
 
@@ -72,6 +99,17 @@ def score(q_bits, w, k_bits, page_table, seq_lens) -> np.ndarray:
     q_bits uint16 [B, H, D]; w float32 [B, H]; k_bits uint16 [P, 64, D];
     page_table int32 [B, max_pages]; seq_lens int32 [B].
     """
+    return score_keys(q_bits, w, bf16_pages(k_bits), k_bits.shape[0], page_table, seq_lens)
+
+
+def score_fp8(q_bits, w, k8, k_scale, page_table, seq_lens) -> np.ndarray:
+    """``score`` with fp8 keys: k8 uint8 [P, 64, D] e4m3fn codes, k_scale
+    float32 [P, 64]; the key of a position is k_scale * decode(k8)."""
+    return score_keys(q_bits, w, fp8_pages(k8, k_scale), k8.shape[0], page_table, seq_lens)
+
+
+def score_keys(q_bits, w, decode, num_pages, page_table, seq_lens) -> np.ndarray:
+    """``score`` over a key pool given by its page decoder."""
     q = bf16_bits_to_f64(q_bits)
     w64 = np.asarray(w, dtype=np.float64)
     B = q.shape[0]
@@ -81,7 +119,7 @@ def score(q_bits, w, k_bits, page_table, seq_lens) -> np.ndarray:
         L = clamp_len(seq_lens[b], N)
         if L == 0:
             continue
-        keys, bad = gather_keys(k_bits, page_table[b], L)
+        keys, bad = gather_keys(decode, num_pages, page_table[b], L)
         dots = q[b] @ keys.T  # [H, L]: every head's dot product with every key
         relu = np.maximum(dots, 0.0)
         row = w64[b] @ relu  # sum over heads of w_h * ReLU(dot_h)
@@ -99,7 +137,7 @@ def score_at(q_bits, w, k_bits, page_table, seq_lens, b: int, s: int) -> float:
     p = int(page_table[b, s // PAGE])
     if p < 0 or p >= k_bits.shape[0]:
         return float("nan")
-    key = bf16_bits_to_f64(k_bits[p, s % PAGE])
+    key = bf16_pages(k_bits)(np.array([p]))[0, s % PAGE]
     q = bf16_bits_to_f64(q_bits[b])
     dots = q @ key
     return float(np.dot(np.asarray(w[b], dtype=np.float64), np.maximum(dots, 0.0)))
@@ -113,6 +151,16 @@ def score_magnitudes(q_bits, w, k_bits, page_table, seq_lens):
     A[b,s] = sum_h |w_h| * sum_d |q_hd * k_sd|    (size of the products)
     Both are 0 at masked positions.
     """
+    return magnitudes_keys(q_bits, w, bf16_pages(k_bits), k_bits.shape[0], page_table, seq_lens)
+
+
+def score_magnitudes_fp8(q_bits, w, k8, k_scale, page_table, seq_lens):
+    """``score_magnitudes`` with fp8 keys (on the scaled keys)."""
+    return magnitudes_keys(q_bits, w, fp8_pages(k8, k_scale), k8.shape[0], page_table, seq_lens)
+
+
+def magnitudes_keys(q_bits, w, decode, num_pages, page_table, seq_lens):
+    """``score_magnitudes`` over a key pool given by its page decoder."""
     q = bf16_bits_to_f64(q_bits)
     w64 = np.abs(np.asarray(w, dtype=np.float64))
     B = q.shape[0]
@@ -123,7 +171,7 @@ def score_magnitudes(q_bits, w, k_bits, page_table, seq_lens):
         L = clamp_len(seq_lens[b], N)
         if L == 0:
             continue
-        keys, _ = gather_keys(k_bits, page_table[b], L)
+        keys, _ = gather_keys(decode, num_pages, page_table[b], L)
         M[b, :L] = w64[b] @ np.abs(q[b] @ keys.T)
         A[b, :L] = w64[b] @ (np.abs(q[b]) @ np.abs(keys).T)
     return M, A

@@ -17,6 +17,12 @@ N(0, 1/32) or |N(0, 1)| / sqrt(32). Lengths are drawn directly in c4 positions,
 uniform over the integer range, which equals a uniform token length that is a
 multiple of 4. Draw order from ``numpy.random.Generator(PCG64(seed))``:
 lengths, page permutation, q, w, k.
+
+fp8 keys (an input format, not a step of the method): the same bfloat16 keys
+are quantized per position to OCP FP8 E4M3 (``e4m3fn``: 4 exponent bits with
+bias 7, 3 mantissa bits, no infinities, largest finite value 448) with a
+float32 scale per position, scale = max_d |k_d| / 448 (1 for an all-zero
+key), codes = round-to-nearest-even(k / scale).
 """
 from __future__ import annotations
 
@@ -81,10 +87,12 @@ class Inputs:
 
     q_bits: np.ndarray
     w: np.ndarray
-    k_bits: np.ndarray
+    k_bits: np.ndarray | None  # None when the keys are fp8
     page_table: np.ndarray
     seq_lens: np.ndarray
     topk: int
+    k8: np.ndarray | None = None  # uint8 [num_pages, PAGE, DIM] e4m3fn codes, dim fastest
+    k_scale: np.ndarray | None = None  # float32 [num_pages, PAGE] scale of each key
 
     @property
     def batch(self) -> int:
@@ -100,7 +108,11 @@ class Inputs:
 
     @property
     def num_pages(self) -> int:
-        return int(self.k_bits.shape[0])
+        return int((self.k_bits if self.k_bits is not None else self.k8).shape[0])
+
+    @property
+    def fp8(self) -> bool:
+        return self.k8 is not None
 
 
 def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
@@ -111,6 +123,47 @@ def round_to_bf16_bits(x: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
     rounded = u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
     return (rounded >> np.uint32(16)).astype(np.uint16)
+
+
+E4M3_MAX = 448.0
+
+
+def _e4m3_magnitudes() -> np.ndarray:
+    """The 127 non-negative finite e4m3fn values, by code 0x00..0x7E
+    (exponent field e, mantissa m: (m / 8) 2^-6 if e = 0, else (1 + m / 8) 2^(e - 7))."""
+    c = np.arange(127)
+    e, m = c >> 3, c & 7
+    return np.where(e == 0, (m / 8.0) * 2.0 ** -6, (1.0 + m / 8.0) * 2.0 ** (e - 7.0))
+
+
+def round_to_e4m3_codes(x: np.ndarray) -> np.ndarray:
+    """Finite reals -> e4m3fn codes, round to nearest, ties to the even code;
+    magnitudes above 448 saturate to 448 (the encoding has no infinity)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), E4M3_MAX)
+    mags = _e4m3_magnitudes()
+    hi = np.clip(np.searchsorted(mags, a, side="left"), 1, 126)  # mags[hi - 1] < a <= mags[hi], or the ends
+    lo = hi - 1
+    d_lo, d_hi = a - mags[lo], mags[hi] - a
+    pick_hi = (d_hi < d_lo) | ((d_hi == d_lo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a <= 0.0, 0, code)
+    return (code | (np.signbit(x).astype(np.int64) << 7)).astype(np.uint8)
+
+
+def quantize_keys_fp8(k_bits: np.ndarray):
+    """bfloat16 keys [P, PAGE, DIM] -> (e4m3fn codes, per-key float32 scales)."""
+    x = (np.asarray(k_bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+    amax = np.abs(x).max(axis=-1)
+    scale = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    codes = round_to_e4m3_codes(x.astype(np.float64) / scale[..., None].astype(np.float64))
+    return codes, scale
+
+
+def to_fp8(inp: "Inputs") -> "Inputs":
+    """The same step with its keys quantized to e4m3fn with per-key scales."""
+    codes, scale = quantize_keys_fp8(inp.k_bits)
+    return Inputs(inp.q_bits, inp.w, None, inp.page_table, inp.seq_lens, inp.topk, codes, scale)
 
 
 def pages_needed(seq_lens: np.ndarray) -> np.ndarray:

@@ -75,3 +75,27 @@ def test_golden_geometry():
         assert out.shape == (1, positions)
     assert 262144 // 8192 == 32  # the work cut by capping 262144 -> 8192 tokens
     assert wl.CONFIGS["stress1m"].max_c4 == 262144 and wl.CONFIGS["stress8k"].max_c4 == 2048
+
+
+def test_e4m3_encoding_matches_torch():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(3)
+    mags = wl._e4m3_magnitudes()
+    mids = (mags[1:] + mags[:-1]) / 2
+    x = np.concatenate([rng.standard_normal(20000) * 60, mags, -mags, mids, -mids, [0.0, -0.0, 448.0]]).astype(np.float32)
+    mine = wl.round_to_e4m3_codes(x)
+    ref = torch.from_numpy(x).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(mine, ref)
+
+
+def test_e4m3_encoding_saturates():
+    assert wl.round_to_e4m3_codes(np.array([449.0, 1e6, -1e6]))[0] == 0x7E
+    assert wl.round_to_e4m3_codes(np.array([-1e6]))[0] == 0xFE
+
+
+def test_fp8_inputs_layout():
+    inp = wl.to_fp8(wl.generate("tiny"))
+    assert inp.fp8 and inp.k_bits is None
+    assert inp.k8.dtype == np.uint8 and inp.k8.shape == (inp.num_pages, wl.PAGE, wl.DIM)
+    assert inp.k_scale.dtype == np.float32 and inp.k_scale.shape == (inp.num_pages, wl.PAGE)
+    assert np.all(inp.k_scale > 0)
