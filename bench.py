@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--config", default="c3", help="workload name (tiny, c2, c3, stress1m, stress8k, full)")
     ap.add_argument("--rotate", type=int, default=0, help="input copies used round robin (0: enough to exceed 2x the Infinity Cache)")
     ap.add_argument("--hwm", action="store_true", help="incremental -inf tail (row_hwm) instead of the stateless full tail")
+    ap.add_argument("--keys", choices=["bf16", "fp8"], default="bf16",
+                    help="key format: bfloat16, or e4m3fn codes with a float32 scale per key")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -97,7 +99,8 @@ def algorithmic_bytes(inp, hwm: bool) -> dict:
 
     lens = np.clip(inp.seq_lens.astype(np.int64), 0, inp.max_c4)
     pages = wl.pages_needed(lens)
-    k_bytes = int(pages.sum()) * wl.PAGE * wl.DIM * 2
+    per_key = wl.DIM + 4 if inp.fp8 else wl.DIM * 2  # fp8: 64 codes and a float32 scale
+    k_bytes = int(pages.sum()) * wl.PAGE * per_key
     out_positions = inp.batch * inp.max_c4 if not hwm else int((pages * wl.PAGE).sum())
     out_bytes = out_positions * 4
     table_bytes = int(pages.sum()) * 4
@@ -129,9 +132,12 @@ def cpu_baseline(inp, reps: int, total_s: float = 12.0) -> dict:
         sub = inp
         if rows < inp.batch:
             sub = type(inp)(inp.q_bits[:rows], inp.w[:rows], inp.k_bits, inp.page_table[:rows],
-                            inp.seq_lens[:rows], inp.topk)
+                            inp.seq_lens[:rows], inp.topk, inp.k8, inp.k_scale)
         t0 = time.perf_counter()
-        s = oracle.score(sub.q_bits, sub.w, sub.k_bits, sub.page_table, sub.seq_lens)
+        if sub.fp8:
+            s = oracle.score_fp8(sub.q_bits, sub.w, sub.k8, sub.k_scale, sub.page_table, sub.seq_lens)
+        else:
+            s = oracle.score(sub.q_bits, sub.w, sub.k_bits, sub.page_table, sub.seq_lens)
         oracle.topk(s, sub.seq_lens, sub.topk)
         dt = time.perf_counter() - t0
         spent += dt
@@ -170,12 +176,14 @@ def main():
     binding.load()
     cfg = wl.CONFIGS[args.config]
     inp = wl.generate(cfg)
+    if args.keys == "fp8":
+        inp = wl.to_fp8(inp)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
     base = binding.to_device(inp, dev)
     B, N, k = inp.batch, inp.max_c4, inp.topk
-    set_bytes = inp.k_bits.nbytes + B * N * 4
+    set_bytes = (inp.k8.nbytes + inp.k_scale.nbytes if inp.fp8 else inp.k_bits.nbytes) + B * N * 4
     R = args.rotate or min(16, max(2, math.ceil(2 * MALL_BYTES / set_bytes)))
     sets = []
     for r in range(R):
@@ -187,8 +195,12 @@ def main():
         sets.append(t)
 
     def launch_score(t):
-        binding.score(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"], out=t["logits"],
-                      row_hwm=t["hwm"])
+        if inp.fp8:
+            binding.score_fp8(t["q"], t["w"], t["k8"], t["k_scale"], t["page_table"], t["seq_lens"], out=t["logits"],
+                              row_hwm=t["hwm"])
+        else:
+            binding.score(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"], out=t["logits"],
+                          row_hwm=t["hwm"])
 
     def launch_topk(t):
         binding.topk(t["logits"], t["seq_lens"], k, out_idx=t["idx"], out_vals=t["vals"])
@@ -243,7 +255,7 @@ def main():
     alg = algorithmic_bytes(inp, args.hwm)
     achieved = alg["total"] / (score_avg_ms * 1e-3) / 1e9
     k_only = alg["k"] / (score_avg_ms * 1e-3) / 1e9
-    traffic = read_traffic(args.config + ("+hwm" if args.hwm else ""))
+    traffic = read_traffic(args.config + ("+hwm" if args.hwm else "") + ("+fp8" if inp.fp8 else ""))
     roofline = {
         "bound": "hbm", "kernel": "score_kernel", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -272,6 +284,7 @@ def main():
             "topk": k, "seed": cfg.seed, "tail": "incremental (row_hwm)" if args.hwm else "stateless full -inf",
             "input_copies": R, "timing": "hipGraph replay of [score; top-k], HIP events",
             "accumulate": "fp32",
+            "keys": "e4m3fn codes + float32 scale per key" if inp.fp8 else "bf16",
         },
         "roofline": roofline,
         "cpu_baseline": None,

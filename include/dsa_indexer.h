@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define DSA_INDEXER_ABI_VERSION 1
+#define DSA_INDEXER_ABI_VERSION 2
 #define DSA_INDEXER_HEADS 32 /* indexer heads */
 #define DSA_INDEXER_DIM 64   /* head dimension */
 #define DSA_INDEXER_PAGE 64  /* c4 positions per page */
@@ -106,6 +106,27 @@ int dsa_indexer_last_hip_error(void);
 int dsa_indexer_score(const void *q, const float *w, const void *k_pool, int64_t num_pages,
                       const int32_t *page_table, const int32_t *seq_lens, int32_t batch,
                       int32_t max_pages, float *logits, int32_t *row_hwm, hipStream_t stream);
+
+/*
+ * Score step with fp8 keys (page "The Indexer O(max_context) Breakthrough"
+ * mentions an fp8 KV cache; the pages do not say how the indexer's keys are
+ * stored, so this format is a reading, not a page fact): each key is 64 OCP
+ * FP8 E4M3 codes (e4m3fn: bias 7, no infinities, largest value 448; code
+ * 0x7F/0xFF is NaN) and one float32 scale, and the key that enters the
+ * formula is scale * decode(codes). Everything else is as for
+ * dsa_indexer_score, which this mirrors argument for argument:
+ *
+ *   k_pool_fp8 uint8 [num_pages][64][64], 16-byte aligned: codes of page p,
+ *              row i (the key of the position that maps to (p, i)), dims
+ *              contiguous; 4 KiB per page
+ *   k_scale    fp32  [num_pages][64], 4-byte aligned: the scale of each key
+ *
+ * Errors as for dsa_indexer_score (DSA_ERR_NULL also for a NULL k_scale).
+ */
+int dsa_indexer_score_fp8(const void *q, const float *w, const void *k_pool_fp8, const float *k_scale,
+                          int64_t num_pages, const int32_t *page_table, const int32_t *seq_lens,
+                          int32_t batch, int32_t max_pages, float *logits, int32_t *row_hwm,
+                          hipStream_t stream);
 
 /* Bytes of device workspace dsa_indexer_topk needs for these sizes: 0 when
  * max_c4 <= 4096 (the workspace may then be NULL) or the sizes are out of

@@ -50,6 +50,8 @@ def load() -> ctypes.CDLL:
     lib.dsa_indexer_last_hip_error.argtypes = []
     lib.dsa_indexer_score.restype = ctypes.c_int
     lib.dsa_indexer_score.argtypes = [vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, vp]
+    lib.dsa_indexer_score_fp8.restype = ctypes.c_int
+    lib.dsa_indexer_score_fp8.argtypes = [vp, vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, vp]
     lib.dsa_indexer_topk_workspace_bytes.restype = sz
     lib.dsa_indexer_topk_workspace_bytes.argtypes = [i32, i32, i32]
     lib.dsa_indexer_topk.restype = ctypes.c_int
@@ -121,6 +123,35 @@ def score(q, w, k_pool, page_table, seq_lens, out=None, row_hwm=None, stream=Non
     return out
 
 
+def score_fp8(q, w, k8, k_scale, page_table, seq_lens, out=None, row_hwm=None, stream=None):
+    """``score`` with fp8 keys: k8 uint8 [num_pages,64,64] e4m3fn codes and
+    k_scale float32 [num_pages,64], one scale per key (see the header)."""
+    import torch
+
+    B, S = page_table.shape
+    dev = q.device
+    _check(q, "q", (torch.bfloat16, torch.int16), (B, HEADS, DIM))
+    _check(w, "w", (torch.float32,), (B, HEADS), dev)
+    _check(k8, "k8", (torch.uint8, torch.int8), None, dev)
+    if k8.dim() != 3 or tuple(k8.shape[1:]) != (PAGE, DIM):
+        raise ValueError(f"k8 has shape {tuple(k8.shape)}, expected [num_pages, {PAGE}, {DIM}]")
+    _check(k_scale, "k_scale", (torch.float32,), (k8.shape[0], PAGE), dev)
+    _check(page_table, "page_table", (torch.int32,), None, dev)
+    _check(seq_lens, "seq_lens", (torch.int32,), (B,), dev)
+    if out is None:
+        out = torch.empty((B, S * PAGE), dtype=torch.float32, device=dev)
+    _check(out, "out", (torch.float32,), (B, S * PAGE), dev)
+    if row_hwm is not None:
+        _check(row_hwm, "row_hwm", (torch.int32,), (B,), dev)
+    st = load().dsa_indexer_score_fp8(
+        q.data_ptr(), w.data_ptr(), k8.data_ptr(), k_scale.data_ptr(), k8.shape[0], page_table.data_ptr(),
+        seq_lens.data_ptr(), B, S, out.data_ptr(), row_hwm.data_ptr() if row_hwm is not None else None,
+        _stream_ptr(stream))
+    if st != 0:
+        raise DsaError(st, "dsa_indexer_score_fp8")
+    return out
+
+
 def topk_workspace_bytes(batch: int, max_c4: int, k: int) -> int:
     return int(load().dsa_indexer_topk_workspace_bytes(batch, max_c4, k))
 
@@ -177,10 +208,15 @@ def to_device(inp, device="cuda"):
     """Upload a ``workloads.Inputs`` to the GPU as the tensors ``score`` takes."""
     import torch
 
-    return {
+    t = {
         "q": torch.from_numpy(inp.q_bits.view("int16")).to(device).view(torch.bfloat16),
         "w": torch.from_numpy(inp.w).to(device),
-        "k_pool": torch.from_numpy(inp.k_bits.view("int16")).to(device).view(torch.bfloat16),
         "page_table": torch.from_numpy(inp.page_table).to(device),
         "seq_lens": torch.from_numpy(inp.seq_lens).to(device),
     }
+    if inp.k_bits is not None:
+        t["k_pool"] = torch.from_numpy(inp.k_bits.view("int16")).to(device).view(torch.bfloat16)
+    if inp.k8 is not None:
+        t["k8"] = torch.from_numpy(inp.k8).to(device)
+        t["k_scale"] = torch.from_numpy(inp.k_scale).to(device)
+    return t

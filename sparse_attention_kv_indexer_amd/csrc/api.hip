@@ -52,7 +52,21 @@ int dsa_indexer_score(const void* q, const float* w, const void* k_pool, int64_t
   if (misaligned16(q) || misaligned16(w) || misaligned16(k_pool) || misaligned16(logits) ||
       misaligned4(page_table) || misaligned4(seq_lens) || misaligned4(row_hwm))
     return DSA_ERR_ALIGN;
-  return from_hip(dsa::launch_score(q, w, k_pool, num_pages, page_table, seq_lens, batch, max_pages,
+  return from_hip(dsa::launch_score(q, w, k_pool, nullptr, num_pages, page_table, seq_lens, batch, max_pages,
+                                    logits, row_hwm, stream));
+}
+
+int dsa_indexer_score_fp8(const void* q, const float* w, const void* k_pool_fp8, const float* k_scale,
+                          int64_t num_pages, const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
+                          int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream) {
+  if (!q || !w || !k_pool_fp8 || !k_scale || !page_table || !seq_lens || !logits) return DSA_ERR_NULL;
+  if (batch < 1 || batch > kMaxBatch || max_pages < 1 || max_pages > kMaxPages || num_pages < 1 ||
+      (int64_t)batch * max_pages > kMaxSlots)
+    return DSA_ERR_SHAPE;
+  if (misaligned16(q) || misaligned16(w) || misaligned16(k_pool_fp8) || misaligned16(logits) ||
+      misaligned4(k_scale) || misaligned4(page_table) || misaligned4(seq_lens) || misaligned4(row_hwm))
+    return DSA_ERR_ALIGN;
+  return from_hip(dsa::launch_score(q, w, k_pool_fp8, k_scale, num_pages, page_table, seq_lens, batch, max_pages,
                                     logits, row_hwm, stream));
 }
 

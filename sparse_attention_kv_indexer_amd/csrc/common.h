@@ -36,8 +36,9 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 constexpr int32_t kMaxRowPositions = 1 << 28;
 
 // Enqueue the score kernel (and, with row_hwm, the high-water-mark update).
-hipError_t launch_score(const void* q, const float* w, const void* k_pool, int64_t num_pages,
-                        const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
+// k_scale == nullptr: bfloat16 keys; otherwise e4m3fn keys with these per-key scales.
+hipError_t launch_score(const void* q, const float* w, const void* k_pool, const float* k_scale,
+                        int64_t num_pages, const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
                         int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream);
 
 // 32-bit words of top-k workspace for these sizes.

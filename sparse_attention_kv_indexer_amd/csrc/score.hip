@@ -33,6 +33,13 @@
 // 32 heads are summed in registers, and one cross-half lane exchange adds the
 // other 16 heads. The tail is written with 16-byte stores, 1 KiB per wave
 // instruction.
+//
+// fp8 keys (score_kernel<true>): a page is 4 KiB of OCP FP8 E4M3 codes plus
+// one float32 scale per key. The codes are staged in LDS under an XOR swizzle
+// of 8-byte chunks and converted to bfloat16 as the MFMA operand is read (the
+// conversion is exact: every e4m3 value is a bfloat16 value); the dot
+// products are then multiplied by their key's scale before the ReLU, which is
+// the formula on the scaled key.
 #include "common.h"
 
 namespace dsa {
@@ -122,10 +129,43 @@ __device__ __forceinline__ void window_find(Window& W, uint32_t item, const Shap
   j = r - (uint32_t)__builtin_amdgcn_readlane((int)W.pre, l);
 }
 
+// Key page format: bfloat16 (8 KiB per page) or fp8 e4m3fn codes (4 KiB)
+// with one float32 scale per key.
+template <bool kFp8>
+struct KeyFormat {
+  static constexpr int kBytes = kFp8 ? kPageBytes / 2 : kPageBytes;  // key bytes per page
+  static constexpr int kLoads = kBytes / 1024;                        // 16-byte loads per lane
+};
+// One page in flight: its key chunks and (fp8) the scales of this lane's two keys.
+template <bool kFp8>
+struct PageRegs {
+  u32x4 v[KeyFormat<kFp8>::kLoads];
+  float s0, s1;
+};
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// 8 e4m3fn codes (bytes of x, lowest first) -> 8 bfloat16 (exact)
+__device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 x) {
+  u32x4 r;
+  r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, false));
+  r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[0], 1.0f, true));
+  r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, false));
+  r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(x[1], 1.0f, true));
+  return __builtin_bit_cast(bf16x8, r);
+}
+
+// LDS 8-byte slot of chunk `j` (0..7, 8 dims each) of fp8 key row `row`:
+// XOR-ing the chunk with the row keeps the rows read by consecutive lanes on
+// distinct banks.
+__device__ __forceinline__ int lds_slot8(int row, int j) { return row * 8 + (j ^ (row & 7)); }
+
+template <bool kFp8>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void score_kernel(
     const uint16_t* __restrict__ q,          // bf16 [B][32][64]
     const float* __restrict__ w,             // [B][32]
-    const uint16_t* __restrict__ k_pool,     // bf16 [num_pages][64][64]
+    const void* __restrict__ k_pool,         // bf16 [num_pages][64][64], or e4m3fn codes [num_pages][64][64]
+    const float* __restrict__ k_scale,       // fp8 only: [num_pages][64]
     int64_t num_pages,
     const int32_t* __restrict__ page_table,  // [B][max_pages]
     const int32_t* __restrict__ seq_lens,    // [B]
@@ -152,7 +192,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void
   const uint32_t s = blockIdx.x * per, e = min(total, s + per);
   if (s >= e) return;
 
-  __shared__ u32x4 tile[kPageChunks];
+  using Fmt = KeyFormat<kFp8>;
+  using Regs = PageRegs<kFp8>;
+  __shared__ u32x4 tile[kPageChunks];  // one bf16 page, or the first half for fp8
   if (s < n_pages) {
     const uint32_t pe = min(e, n_pages);
     Window W{0, 0, 0, 0, 0};
@@ -169,6 +211,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void
     // zeros without a memory access), so the compiler's in-order wait counts
     // never fall back to waiting for everything in flight.
     const rsrc_t none = make_rsrc(k_pool, 0u);
+    const char* const kbase = static_cast<const char*>(k_pool);
     // page id load of item x (pending until key_load reads it); 0 past the range
     auto id_load = [&](uint32_t x, int& bx, uint32_t& jx) -> uint32_t {
       const bool in = x < pe;
@@ -178,13 +221,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void
     };
     // key page of a loaded id into dst; false if the id is outside the pool
     // (then dst is zero and the page is never dereferenced)
-    auto key_load = [&](uint32_t id, u32x4 (&dst)[8]) -> bool {
+    auto key_load = [&](uint32_t id, Regs& dst) -> bool {
       const int page = __builtin_amdgcn_readfirstlane((int)id);
       const bool ok = page >= 0 && (int64_t)page < num_pages;
-      const rsrc_t kp = ok ? make_rsrc(k_pool + (int64_t)page * (kPage * kDim), kPageBytes) : none;
-      // 16-byte chunk c = 64 * i + lane is key row c / 8, column c % 8
+      const rsrc_t kp = ok ? make_rsrc(kbase + (int64_t)page * Fmt::kBytes, Fmt::kBytes) : none;
+      // 16-byte chunk c = 64 * i + lane of the page
 #pragma unroll
-      for (int i = 0; i < 8; ++i) dst[i] = __builtin_amdgcn_raw_buffer_load_b128(kp, (i * 64 + lane) * 16, 0, kNonTemporal);
+      for (int i = 0; i < Fmt::kLoads; ++i)
+        dst.v[i] = __builtin_amdgcn_raw_buffer_load_b128(kp, (i * 64 + lane) * 16, 0, kNonTemporal);
+      if constexpr (kFp8) {
+        // scales of this lane's keys n and n + 32
+        const rsrc_t sp = ok ? make_rsrc(k_scale + (int64_t)page * kPage, kPage * 4u) : none;
+        dst.s0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sp, n * 4, 0, 0));
+        dst.s1 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sp, (n + 32) * 4, 0, 0));
+      }
       return ok;
     };
 
@@ -212,25 +262,58 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void
       }
     };
     // scores of item (bx, jx) from its key page (q and w of bx held)
-    auto compute = [&](int bx, uint32_t jx, bool okx, const u32x4 (&page)[8]) {
+    auto compute = [&](int bx, uint32_t jx, bool okx, const Regs& page) {
       const int len = clamp_len(seq_lens[bx], sh.width);
       const int base = (int)jx * kPage;
       float val = __builtin_nanf("");  // a page id outside the pool scores NaN
       if (okx) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) tile[lds_slot(i * 8 + (lane >> 3), lane & 7)] = page[i];
-        __syncthreads();
-        // keys operand B (16 dims x 32 positions per step): lane holds position
-        // n of the half page, dims 16*kb + 8*half .. +7
         f32x16 acc0 = {};  // positions 0..31 of the page
         f32x16 acc1 = {};  // positions 32..63
+        if constexpr (!kFp8) {
+          // 16-byte chunk c = 64 * i + lane is key row c / 8, column c % 8
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const int col = 2 * kb + half;
-          const bf16x8 b0 = __builtin_bit_cast(bf16x8, tile[lds_slot(n, col)]);
-          const bf16x8 b1 = __builtin_bit_cast(bf16x8, tile[lds_slot(n + 32, col)]);
-          acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b0, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b1, acc1, 0, 0, 0);
+          for (int i = 0; i < Fmt::kLoads; ++i) tile[lds_slot(i * 8 + (lane >> 3), lane & 7)] = page.v[i];
+          __syncthreads();
+          // keys operand B (16 dims x 32 positions per step): lane holds position
+          // n of the half page, dims 16*kb + 8*half .. +7
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const int col = 2 * kb + half;
+            const bf16x8 b0 = __builtin_bit_cast(bf16x8, tile[lds_slot(n, col)]);
+            const bf16x8 b1 = __builtin_bit_cast(bf16x8, tile[lds_slot(n + 32, col)]);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b0, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b1, acc1, 0, 0, 0);
+          }
+        } else {
+          // 16-byte chunk c = 64 * i + lane is key row c / 4, dims 16 * (c % 4) .. +15:
+          // two 8-byte chunks, stored at their swizzled slots
+          u32x2* tile8 = reinterpret_cast<u32x2*>(tile);
+#pragma unroll
+          for (int i = 0; i < Fmt::kLoads; ++i) {
+            const int c = i * 64 + lane, row = c >> 2, j = 2 * (c & 3);
+            u32x2 lo, hi;
+            lo[0] = page.v[i][0];
+            lo[1] = page.v[i][1];
+            hi[0] = page.v[i][2];
+            hi[1] = page.v[i][3];
+            tile8[lds_slot8(row, j)] = lo;
+            tile8[lds_slot8(row, j + 1)] = hi;
+          }
+          __syncthreads();
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const int j = 2 * kb + half;
+            const bf16x8 b0 = e4m3x8_to_bf16(tile8[lds_slot8(n, j)]);
+            const bf16x8 b1 = e4m3x8_to_bf16(tile8[lds_slot8(n + 32, j)]);
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b0, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b1, acc1, 0, 0, 0);
+          }
+          // each dot product times its key's scale (this lane's keys n and n + 32)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            acc0[r] *= page.s0;
+            acc1[r] *= page.s1;
+          }
         }
         __syncthreads();  // the tile is rewritten for the next page
         // weighted ReLU over this lane's 16 heads, then the other 16 from lane ^ 32
@@ -255,7 +338,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void
 
     // state at the top of each half of the loop, for the item `it` it computes:
     // its keys in KA (phase A) or KB (phase B), the id of it + 1 in flight
-    u32x4 KA[8], KB[8];
+    Regs KA, KB;
     int bA = 0, bB = 0, bX = 0, bY = 0;
     uint32_t jA = 0, jB = 0, jX = 0, jY = 0, PX = 0, PY = 0;
     bool okA = false, okB = false;
@@ -334,17 +417,20 @@ int cu_count(hipStream_t stream) {
 
 }  // namespace
 
-hipError_t launch_score(const void* q, const float* w, const void* k_pool, int64_t num_pages,
-                        const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
+hipError_t launch_score(const void* q, const float* w, const void* k_pool, const float* k_scale,
+                        int64_t num_pages, const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
                         int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream) {
   // as many one-wave workgroups as stay resident, but no more than the largest
   // list these shapes allow (every slot a page, plus every tail chunk)
   const int64_t width = (int64_t)max_pages * kPage;
   const int64_t most = (int64_t)batch * max_pages + (int64_t)batch * ((width + kTailChunk - 1) / kTailChunk);
   const int grid = (int)std::min<int64_t>((int64_t)cu_count(stream) * kWavesPerCU, most);
-  hipLaunchKernelGGL(score_kernel, dim3(grid), dim3(64), 0, stream, static_cast<const uint16_t*>(q), w,
-                     static_cast<const uint16_t*>(k_pool), num_pages, page_table, seq_lens, batch, max_pages,
-                     logits, row_hwm);
+  if (k_scale != nullptr)
+    hipLaunchKernelGGL(score_kernel<true>, dim3(grid), dim3(64), 0, stream, static_cast<const uint16_t*>(q), w, k_pool,
+                       k_scale, num_pages, page_table, seq_lens, batch, max_pages, logits, row_hwm);
+  else
+    hipLaunchKernelGGL(score_kernel<false>, dim3(grid), dim3(64), 0, stream, static_cast<const uint16_t*>(q), w, k_pool,
+                       k_scale, num_pages, page_table, seq_lens, batch, max_pages, logits, row_hwm);
   if (row_hwm != nullptr) {
     // after every workgroup of the score kernel has read the old marks
     hipLaunchKernelGGL(hwm_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, seq_lens, batch,

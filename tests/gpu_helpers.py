@@ -20,7 +20,10 @@ def run_score(lib, inp, poison_out=True, device="cuda"):
     out = torch.empty((inp.batch, inp.max_c4), dtype=torch.float32, device=device)
     if poison_out:
         out.fill_(float("nan"))  # unwritten positions would show up as NaN
-    lib.score(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"], out=out)
+    if inp.fp8:
+        lib.score_fp8(t["q"], t["w"], t["k8"], t["k_scale"], t["page_table"], t["seq_lens"], out=out)
+    else:
+        lib.score(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"], out=out)
     torch.cuda.synchronize()
     return out.cpu().numpy(), t, out
 
@@ -34,8 +37,12 @@ def run_topk(lib, logits_dev, seq_lens_dev, k, with_values=True):
 
 
 def oracle_scores(inp):
-    ref = oracle.score(inp.q_bits, inp.w, inp.k_bits, inp.page_table, inp.seq_lens)
-    M, A = oracle.score_magnitudes(inp.q_bits, inp.w, inp.k_bits, inp.page_table, inp.seq_lens)
+    if inp.fp8:
+        ref = oracle.score_fp8(inp.q_bits, inp.w, inp.k8, inp.k_scale, inp.page_table, inp.seq_lens)
+        M, A = oracle.score_magnitudes_fp8(inp.q_bits, inp.w, inp.k8, inp.k_scale, inp.page_table, inp.seq_lens)
+    else:
+        ref = oracle.score(inp.q_bits, inp.w, inp.k_bits, inp.page_table, inp.seq_lens)
+        M, A = oracle.score_magnitudes(inp.q_bits, inp.w, inp.k_bits, inp.page_table, inp.seq_lens)
     return ref, M, A
 
 

@@ -29,13 +29,13 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 6, names
+    assert len(names) == 7, names
     for name in names:
         assert hasattr(lib, name), f"{name} not exported"
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dsa_indexer_abi_version() == 1
+    assert lib.dsa_indexer_abi_version() == 2
     for st in (OK, NULL, SHAPE, ALIGN, K, WS, -6):
         assert lib.dsa_indexer_status_string(st).decode() not in ("", "unknown status")
     assert lib.dsa_indexer_status_string(12345).decode() == "unknown status"
@@ -98,3 +98,26 @@ def test_topk_workspace_contract(lib):
     assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=32768, k=2048, workspace=A, ws_bytes=need - 1)) == WS
     assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=32768, k=2048, workspace=None, ws_bytes=need)) == WS
     assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=32768, k=2048, workspace=A + 4, ws_bytes=need)) == ALIGN
+
+
+def score_fp8_args(**over):
+    args = dict(q=A, w=A, k_pool_fp8=A, k_scale=A, num_pages=4, page_table=A, seq_lens=A, batch=2, max_pages=3,
+                logits=A, row_hwm=None, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("field", ["q", "w", "k_pool_fp8", "k_scale", "page_table", "seq_lens", "logits"])
+def test_score_fp8_null(lib, field):
+    assert lib.dsa_indexer_score_fp8(*score_fp8_args(**{field: None})) == NULL
+
+
+@pytest.mark.parametrize("over", [dict(batch=0), dict(batch=65536), dict(max_pages=0), dict(max_pages=(1 << 22) + 1),
+                                  dict(num_pages=0)])
+def test_score_fp8_shape(lib, over):
+    assert lib.dsa_indexer_score_fp8(*score_fp8_args(**over)) == SHAPE
+
+
+@pytest.mark.parametrize("field,off", [("q", 8), ("k_pool_fp8", 4), ("k_scale", 2), ("logits", 4), ("page_table", 2)])
+def test_score_fp8_alignment(lib, field, off):
+    assert lib.dsa_indexer_score_fp8(*score_fp8_args(**{field: A + off})) == ALIGN
