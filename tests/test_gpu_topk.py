@@ -144,3 +144,39 @@ def test_large_batch(lib):
     xd, ld = _upload(x, lens)
     idx, vals = run_topk(lib, xd, ld, k)
     check_topk_exact(idx, vals, x, lens, k)
+
+
+def test_segment_cut_above_kth_falls_back(lib):
+    """One segment holds every large score, so its share of the top k is far
+    above the average its cut aims at: its cut lies above the k-th largest key,
+    and the row kernel must select over the whole row instead."""
+    rng = np.random.default_rng(14)
+    B, N, k = 2, 16384, 2048
+    x = rng.standard_normal((B, N)).astype(np.float32)
+    x[0, :4096] = 1000.0 + rng.random(4096).astype(np.float32)
+    x[1, 8192:12288] = 50.0 + np.round(rng.random(4096) * 8).astype(np.float32)  # ties among the large ones
+    lens = np.array([16384, 16000])
+    say("topk segment cut above the k-th key")
+    xd, ld = _upload(x, lens)
+    idx, vals = run_topk(lib, xd, ld, k)
+    check_topk_exact(idx, vals, x, lens, k)
+
+
+def test_too_few_candidates_falls_back(lib):
+    """Large scores exactly at the segment kernel's sampled slots (lane t of a
+    4096-position segment samples offsets 16t + (t % 16) and
+    16t + ((t + 8) % 16)) make every segment's cut keep little more than the
+    samples; with k above their total the row kernel must select over the
+    whole row."""
+    rng = np.random.default_rng(15)
+    B, N, k = 2, 32768, 5000
+    x = rng.standard_normal((B, N)).astype(np.float32)
+    t = np.arange(256)
+    for s0 in range(0, N, 4096):
+        for off in (16 * t + (t % 16), 16 * t + ((t + 8) % 16)):
+            x[:, s0 + off] = 500.0 + rng.random(256).astype(np.float32)
+    lens = np.array([32768, 30000])
+    say("topk too few candidates")
+    xd, ld = _upload(x, lens)
+    idx, vals = run_topk(lib, xd, ld, k)
+    check_topk_exact(idx, vals, x, lens, k)
