@@ -208,3 +208,50 @@ def topk_values(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
         sel = idx[b] >= 0
         vals[b, sel] = logits[b, idx[b, sel]]
     return vals
+
+
+# ---------------------------------------------------------------------------
+# Sparse attention over the selected positions (the step after the indexer)
+# ---------------------------------------------------------------------------
+#
+# Page "The Indexer O(max_context) Breakthrough", sections "Phase 1: The MMA
+# Sparse-MLA Decode Kernel" and "Phase 2: Split-K Parallelization" (and the
+# kernel list in "The Profile: Proof in the GPU Timeline" of "The O(Actual)
+# Indexer: Validating 128K Context"): the decode attention reads the KV
+# entries of the positions the indexer selected (MLA: one latent entry shared
+# by all heads), computes each head's softmax attention over them, and may
+# split the selected set into parts whose partial results are combined by a
+# log-sum-exp merge. Readings (the pages give no sizes): per position one
+# latent of KD = 576 dims (the first VD = 512 of which are the value), per
+# request H query vectors of KD dims, a caller-given softmax scale; positions
+# marked -1 are not attended; a request with none gives output 0 and
+# log-sum-exp -inf.
+
+def sparse_attention(q_bits, kv_bits, page_table, idx, scale: float, vd: int):
+    """Output [B, H, vd] and natural-log LSE [B, H] in float64.
+
+    q_bits uint16 [B, H, KD] bfloat16 queries; kv_bits uint16 [P, 64, KD]
+    bfloat16 latents (page p, row i: the latent of the position that maps to
+    (p, i)); page_table int32 [B, max_pages]; idx int [B, k] positions (any
+    order; -1 = none); the score of position s for head h is
+    scale * q[b, h] . kv[s], its weight softmax over the request's positions,
+    and the output sum_s weight * kv[s, :vd].
+    """
+    q = bf16_bits_to_f64(q_bits)
+    B, H, KD = q.shape
+    out = np.zeros((B, H, vd))
+    lse = np.full((B, H), -np.inf)
+    for b in range(B):
+        pos = np.asarray([int(s) for s in idx[b] if s >= 0], dtype=np.int64)
+        if pos.size == 0:
+            continue
+        pages = np.asarray(page_table[b], dtype=np.int64)[pos // PAGE]
+        lat = bf16_bits_to_f64(kv_bits[pages, pos % PAGE])  # [n, KD]
+        s = scale * (q[b] @ lat.T)  # [H, n]
+        m = s.max(axis=1, keepdims=True)
+        e = np.exp(s - m)
+        l = e.sum(axis=1, keepdims=True)
+        out[b] = (e / l) @ lat[:, :vd]
+        lse[b] = (m + np.log(l))[:, 0]
+    return out, lse
+

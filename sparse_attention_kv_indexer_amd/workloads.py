@@ -243,3 +243,34 @@ def random_case(seed: int, batch: int, max_pages: int, lens=None, topk: int = 16
         w = np.abs(w)
     k = _normal_bf16(rng, (num_pages, PAGE, DIM))
     return Inputs(q, w.astype(np.float32), k, table, lens, topk)
+
+
+# Sparse attention after the indexer (an input recipe for the step that reads
+# the selected positions): per position one bfloat16 latent of ATT_KD dims
+# (the first ATT_VD of which are the value), ATT_HEADS bfloat16 queries of
+# ATT_KD dims per request, all N(0, 1); scale 1 / sqrt(192). Drawn from their
+# own stream, PCG64(seed + ATT_SEED_OFFSET): queries, then latents, so the
+# indexer's inputs are unchanged.
+ATT_HEADS = 32
+ATT_KD = 576
+ATT_VD = 512
+ATT_SCALE = 1.0 / math.sqrt(192.0)
+ATT_SEED_OFFSET = 1000
+
+
+@dataclasses.dataclass
+class AttentionInputs:
+    """q_bits uint16 [B, ATT_HEADS, ATT_KD]; kv_bits uint16 [num_pages, PAGE, ATT_KD]
+    (same pages and page table as the indexer's keys); scale float."""
+
+    q_bits: np.ndarray
+    kv_bits: np.ndarray
+    scale: float
+
+
+def attention_inputs(inp: Inputs, seed: int) -> AttentionInputs:
+    rng = np.random.Generator(np.random.PCG64(seed + ATT_SEED_OFFSET))
+    q = _normal_bf16(rng, (inp.batch, ATT_HEADS, ATT_KD))
+    kv = _normal_bf16(rng, (inp.num_pages, PAGE, ATT_KD))
+    return AttentionInputs(q, kv, ATT_SCALE)
+

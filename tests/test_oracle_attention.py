@@ -1,0 +1,99 @@
+"""Pins of the oracle's sparse attention over the selected positions (CPU):
+a pure-Python brute force, closed forms, invariance to the order of the
+selection, and the log-sum-exp merge of a split selection."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from sparse_attention_kv_indexer_amd import workloads as wl
+
+
+def _case(seed, B=3, H=4, KD=8, S=3, k=10):
+    rng = np.random.default_rng(seed)
+    inp = wl.random_case(seed, B, S, lens=[S * 64] * B)
+    q = wl.round_to_bf16_bits(rng.standard_normal((B, H, KD)).astype(np.float32))
+    kv = wl.round_to_bf16_bits(rng.standard_normal((inp.num_pages, wl.PAGE, KD)).astype(np.float32))
+    idx = np.stack([rng.choice(S * 64, size=k, replace=False) for _ in range(B)]).astype(np.int64)
+    return inp, q, kv, idx
+
+
+def test_brute_force_small():
+    inp, q, kv, idx = _case(0)
+    scale, vd = 0.37, 6
+    out, lse = oracle.sparse_attention(q, kv, inp.page_table, idx, scale, vd)
+    qf = oracle.bf16_bits_to_f64(q)
+    kf = oracle.bf16_bits_to_f64(kv)
+    for b in range(q.shape[0]):
+        for h in range(q.shape[1]):
+            rows = [kf[inp.page_table[b, s // 64], s % 64] for s in idx[b]]
+            sc = [scale * math.fsum(float(qf[b, h, d]) * float(r[d]) for d in range(q.shape[2])) for r in rows]
+            m = max(sc)
+            ws = [math.exp(x - m) for x in sc]
+            tot = math.fsum(ws)
+            assert lse[b, h] == pytest.approx(m + math.log(tot), rel=1e-13, abs=1e-13)
+            for d in range(vd):
+                ref = math.fsum(w_ * float(r[d]) for w_, r in zip(ws, rows)) / tot
+                assert out[b, h, d] == pytest.approx(ref, rel=1e-12, abs=1e-13)
+
+
+def test_single_position_returns_its_value():
+    inp, q, kv, idx = _case(1, k=10)
+    idx[:, 1:] = -1
+    out, lse = oracle.sparse_attention(q, kv, inp.page_table, idx, 0.5, 6)
+    kf = oracle.bf16_bits_to_f64(kv)
+    qf = oracle.bf16_bits_to_f64(q)
+    for b in range(idx.shape[0]):
+        s = idx[b, 0]
+        lat = kf[inp.page_table[b, s // 64], s % 64]
+        assert np.array_equal(out[b], np.broadcast_to(lat[:6], out[b].shape))
+        assert np.allclose(lse[b], 0.5 * (qf[b] @ lat), rtol=0, atol=1e-12)
+
+
+def test_zero_query_averages_the_values():
+    inp, q, kv, idx = _case(2)
+    q[:] = 0
+    out, lse = oracle.sparse_attention(q, kv, inp.page_table, idx, 1.0, 8)
+    kf = oracle.bf16_bits_to_f64(kv)
+    for b in range(idx.shape[0]):
+        lat = np.stack([kf[inp.page_table[b, s // 64], s % 64] for s in idx[b]])
+        assert np.allclose(out[b], lat.mean(axis=0), rtol=0, atol=1e-13)
+        assert np.allclose(lse[b], math.log(idx.shape[1]), rtol=0, atol=1e-13)
+
+
+def test_order_of_selection_does_not_matter():
+    inp, q, kv, idx = _case(3)
+    a = oracle.sparse_attention(q, kv, inp.page_table, idx, 0.3, 8)
+    rev = idx[:, ::-1].copy()
+    b = oracle.sparse_attention(q, kv, inp.page_table, rev, 0.3, 8)
+    assert np.allclose(a[0], b[0], rtol=0, atol=1e-13) and np.allclose(a[1], b[1], rtol=0, atol=1e-13)
+
+
+def test_split_selection_merges_by_log_sum_exp():
+    """Attention over a union equals the LSE-weighted merge of its parts."""
+    inp, q, kv, idx = _case(4, k=12)
+    full = oracle.sparse_attention(q, kv, inp.page_table, idx, 0.4, 8)
+    p1 = oracle.sparse_attention(q, kv, inp.page_table, np.where(np.arange(12) < 5, idx, -1), 0.4, 8)
+    p2 = oracle.sparse_attention(q, kv, inp.page_table, np.where(np.arange(12) >= 5, idx, -1), 0.4, 8)
+    m = np.maximum(p1[1], p2[1])
+    w1, w2 = np.exp(p1[1] - m), np.exp(p2[1] - m)
+    merged = (w1[..., None] * p1[0] + w2[..., None] * p2[0]) / (w1 + w2)[..., None]
+    assert np.allclose(merged, full[0], rtol=0, atol=1e-13)
+    assert np.allclose(m + np.log(w1 + w2), full[1], rtol=0, atol=1e-13)
+
+
+def test_empty_selection():
+    inp, q, kv, idx = _case(5)
+    idx[1] = -1
+    out, lse = oracle.sparse_attention(q, kv, inp.page_table, idx, 1.0, 8)
+    assert np.all(out[1] == 0) and np.all(np.isneginf(lse[1]))
+    assert np.all(np.isfinite(lse[0]))
+
+
+def test_generator_shapes():
+    inp = wl.generate("tiny")
+    att = wl.attention_inputs(inp, 0)
+    assert att.q_bits.shape == (1, wl.ATT_HEADS, wl.ATT_KD) and att.q_bits.dtype == np.uint16
+    assert att.kv_bits.shape == (inp.num_pages, wl.PAGE, wl.ATT_KD)
+    assert att.scale == pytest.approx(1 / math.sqrt(192))
