@@ -224,8 +224,10 @@ def topk_values(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
 # log-sum-exp merge. Readings (the pages give no sizes): per position one
 # latent of KD = 576 dims (the first VD = 512 of which are the value), per
 # request H query vectors of KD dims, a caller-given softmax scale; positions
-# marked -1 are not attended; a request with none gives output 0 and
-# log-sum-exp -inf.
+# marked -1 (any negative value) are not attended; a request with none gives
+# output 0 and log-sum-exp -inf; a selected position past the page table, or
+# on a page id outside the pool, makes its request's output and log-sum-exp
+# NaN (the score step flags keys on such pages the same way).
 
 def sparse_attention(q_bits, kv_bits, page_table, idx, scale: float, vd: int):
     """Output [B, H, vd] and natural-log LSE [B, H] in float64.
@@ -239,13 +241,21 @@ def sparse_attention(q_bits, kv_bits, page_table, idx, scale: float, vd: int):
     """
     q = bf16_bits_to_f64(q_bits)
     B, H, KD = q.shape
+    num_pages = kv_bits.shape[0]
+    width = page_table.shape[1] * PAGE
     out = np.zeros((B, H, vd))
     lse = np.full((B, H), -np.inf)
     for b in range(B):
         pos = np.asarray([int(s) for s in idx[b] if s >= 0], dtype=np.int64)
         if pos.size == 0:
             continue
+        if np.any(pos >= width):
+            out[b], lse[b] = np.nan, np.nan
+            continue
         pages = np.asarray(page_table[b], dtype=np.int64)[pos // PAGE]
+        if np.any((pages < 0) | (pages >= num_pages)):
+            out[b], lse[b] = np.nan, np.nan
+            continue
         lat = bf16_bits_to_f64(kv_bits[pages, pos % PAGE])  # [n, KD]
         s = scale * (q[b] @ lat.T)  # [H, n]
         m = s.max(axis=1, keepdims=True)

@@ -97,3 +97,20 @@ def test_generator_shapes():
     assert att.q_bits.shape == (1, wl.ATT_HEADS, wl.ATT_KD) and att.q_bits.dtype == np.uint16
     assert att.kv_bits.shape == (inp.num_pages, wl.PAGE, wl.ATT_KD)
     assert att.scale == pytest.approx(1 / math.sqrt(192))
+
+
+def test_positions_off_the_table_or_pool_poison_only_their_request():
+    inp, q, kv, idx = _case(6, B=4)
+    pt = inp.page_table.copy()
+    idx[1, 3] = pt.shape[1] * 64          # past the page table
+    pt[2, idx[2, 0] // 64] = kv.shape[0]  # page id outside the pool
+    pt[3, idx[3, 0] // 64] = -5
+    out, lse = oracle.sparse_attention(q, kv, pt, idx, 0.5, 8)
+    for b in (1, 2, 3):
+        assert np.all(np.isnan(out[b])) and np.all(np.isnan(lse[b]))
+    assert np.all(np.isfinite(out[0])) and np.all(np.isfinite(lse[0]))
+    # a negative entry is never looked up, whatever its page would be
+    idx2 = idx.copy()
+    idx2[0, 0] = -7
+    out2, _ = oracle.sparse_attention(q, kv, inp.page_table, idx2, 0.5, 8)
+    assert np.all(np.isfinite(out2[0]))
