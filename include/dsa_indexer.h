@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define DSA_INDEXER_ABI_VERSION 2
+#define DSA_INDEXER_ABI_VERSION 3
 #define DSA_INDEXER_HEADS 32 /* indexer heads */
 #define DSA_INDEXER_DIM 64   /* head dimension */
 #define DSA_INDEXER_PAGE 64  /* c4 positions per page */
@@ -168,6 +168,56 @@ size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k
 int dsa_indexer_topk(const float *logits, const int32_t *seq_lens, int32_t batch, int32_t max_c4,
                      int32_t k, int32_t *out_idx, float *out_vals, void *workspace,
                      size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Sparse attention over the selected positions (the step after the indexer;
+ * page "The Indexer O(max_context) Breakthrough", sections "Phase 1: The MMA
+ * Sparse-MLA Decode Kernel" and "Phase 2: Split-K Parallelization").
+ *
+ * For every request b and head h < 32, with the list entries s = idx[b][j]
+ * that are >= 0:
+ *   score_s  = scale * sum_{d<576} q[b][h][d] * kv[s][d]
+ *   out[b][h][v] = sum_s softmax(score)_s * kv[s][v]     for v < 512
+ *   lse[b][h]    = log(sum_s exp(score_s))               (natural log)
+ * where kv[s] is the latent of position s: row s % 64 of page
+ * page_table[b][s / 64]. Each latent (576 bfloat16: the first 512 are the
+ * value, the last 64 only enter the score) is read once per request and
+ * shared by the 32 heads. Products are exact, sums are float32, and the
+ * softmax weights enter the weighted sum of values as bfloat16.
+ *
+ *   q          bf16  [batch][32][576], 16-byte aligned
+ *   kv_pool    bf16  [num_pages][64][576], 16-byte aligned
+ *   num_pages  1 .. 2^26 - 1
+ *   page_table int32 [batch][max_pages] (the indexer's table)
+ *   batch      1 .. 65535;  max_pages 1 .. 2^22
+ *   idx        int32 [batch][k]: positions in any order; negative entries are
+ *              skipped (the -1 padding of dsa_indexer_topk's out_idx)
+ *   k          1 .. 2048
+ *   scale      softmax scale (finite)
+ *   out        fp32 [batch][32][512], 16-byte aligned
+ *   lse        fp32 [batch][32]
+ *   workspace  device buffer, 16-byte aligned, of ws_bytes >=
+ *              dsa_indexer_sparse_attention_workspace_bytes() (may be NULL when
+ *              that is 0); contents on entry do not matter. Overlapping calls
+ *              (other streams) need workspaces of their own
+ *   stream     HIP stream to enqueue on
+ *
+ * Defined outcomes that only the device can see: a request with no entry >= 0
+ * gets out = 0 and lse = -inf; a request with an entry at or past
+ * max_pages * 64, or on a page id outside [0, num_pages), gets NaN in all of
+ * its out and lse (no memory outside the pool is read).
+ *
+ * Each request's list is cut into splits of equal length, planned from
+ * (batch, k) alone; one workgroup per (request, split) computes that split's
+ * softmax-normalised output and log-sum-exp, and with more than one split a
+ * second kernel merges them by their log-sum-exps.
+ */
+size_t dsa_indexer_sparse_attention_workspace_bytes(int32_t batch, int32_t k);
+
+int dsa_indexer_sparse_attention(const void *q, const void *kv_pool, int64_t num_pages,
+                                 const int32_t *page_table, int32_t batch, int32_t max_pages,
+                                 const int32_t *idx, int32_t k, float scale, float *out, float *lse,
+                                 void *workspace, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -14,6 +14,7 @@ import os
 from . import build as _build
 
 HEADS, DIM, PAGE = 32, 64, 64
+ATT_HEADS, ATT_KD, ATT_VD = 32, 576, 512
 
 _STATUS = {0: "DSA_OK", -1: "DSA_ERR_NULL", -2: "DSA_ERR_SHAPE", -3: "DSA_ERR_ALIGN",
            -4: "DSA_ERR_K", -5: "DSA_ERR_WORKSPACE", -6: "DSA_ERR_HIP"}
@@ -56,6 +57,11 @@ def load() -> ctypes.CDLL:
     lib.dsa_indexer_topk_workspace_bytes.argtypes = [i32, i32, i32]
     lib.dsa_indexer_topk.restype = ctypes.c_int
     lib.dsa_indexer_topk.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.dsa_indexer_sparse_attention_workspace_bytes.restype = sz
+    lib.dsa_indexer_sparse_attention_workspace_bytes.argtypes = [i32, i32]
+    lib.dsa_indexer_sparse_attention.restype = ctypes.c_int
+    lib.dsa_indexer_sparse_attention.argtypes = [vp, vp, i64, vp, i32, i32, vp, i32, ctypes.c_float, vp, vp,
+                                                 vp, sz, vp]
     _lib = lib
     return lib
 
@@ -202,6 +208,63 @@ def topk(logits, seq_lens, k, out_idx=None, out_vals=None, with_values=False, wo
     if st != 0:
         raise DsaError(st, "dsa_indexer_topk")
     return out_idx, out_vals
+
+
+def sparse_attention_workspace_bytes(batch: int, k: int) -> int:
+    return int(load().dsa_indexer_sparse_attention_workspace_bytes(batch, k))
+
+
+def sparse_attention(q, kv_pool, page_table, idx, scale, out=None, lse=None, workspace=None, stream=None):
+    """Attention of 32 heads over each request's selected positions.
+
+    q bf16 [B,32,576]; kv_pool bf16 [num_pages,64,576] (latents, the first
+    512 dims the value); page_table int32 [B,max_pages]; idx int32 [B,k]
+    (negative entries skipped); returns out float32 [B,32,512] and the
+    natural-log lse float32 [B,32] (see the header).
+    """
+    import torch
+
+    B, k = idx.shape
+    dev = q.device
+    bf16 = (torch.bfloat16, torch.int16)
+    _check(q, "q", bf16, (B, ATT_HEADS, ATT_KD))
+    _check(kv_pool, "kv_pool", bf16, None, dev)
+    if kv_pool.dim() != 3 or tuple(kv_pool.shape[1:]) != (PAGE, ATT_KD):
+        raise ValueError(f"kv_pool has shape {tuple(kv_pool.shape)}, expected [num_pages, {PAGE}, {ATT_KD}]")
+    _check(page_table, "page_table", (torch.int32,), None, dev)
+    if page_table.dim() != 2 or page_table.shape[0] != B:
+        raise ValueError(f"page_table has shape {tuple(page_table.shape)}, expected [{B}, max_pages]")
+    _check(idx, "idx", (torch.int32,), None, dev)
+    if out is None:
+        out = torch.empty((B, ATT_HEADS, ATT_VD), dtype=torch.float32, device=dev)
+    _check(out, "out", (torch.float32,), (B, ATT_HEADS, ATT_VD), dev)
+    if lse is None:
+        lse = torch.empty((B, ATT_HEADS), dtype=torch.float32, device=dev)
+    _check(lse, "lse", (torch.float32,), (B, ATT_HEADS), dev)
+    need = sparse_attention_workspace_bytes(B, k)
+    if workspace is None and need > 0:
+        key = (str(dev), need)
+        if key not in _workspaces:
+            _workspaces[key] = torch.empty(need, dtype=torch.uint8, device=dev)
+        workspace = _workspaces[key]
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = load().dsa_indexer_sparse_attention(
+        q.data_ptr(), kv_pool.data_ptr(), kv_pool.shape[0], page_table.data_ptr(), B, page_table.shape[1],
+        idx.data_ptr(), k, float(scale), out.data_ptr(), lse.data_ptr(), ws_ptr, ws_bytes, _stream_ptr(stream))
+    if st != 0:
+        raise DsaError(st, "dsa_indexer_sparse_attention")
+    return out, lse
+
+
+def attention_to_device(att, device="cuda"):
+    """Upload a ``workloads.AttentionInputs`` (queries and latents) to the GPU."""
+    import torch
+
+    return {
+        "q": torch.from_numpy(att.q_bits.view("int16")).to(device).view(torch.bfloat16),
+        "kv_pool": torch.from_numpy(att.kv_bits.view("int16")).to(device).view(torch.bfloat16),
+    }
 
 
 def to_device(inp, device="cuda"):

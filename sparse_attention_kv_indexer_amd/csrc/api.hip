@@ -20,6 +20,8 @@ int from_hip(hipError_t e) {
 constexpr int32_t kMaxBatch = 65535;  // grid y / x limit used by the launches
 constexpr int32_t kMaxPages = dsa::kMaxRowPositions / dsa::kPage;
 constexpr int64_t kMaxSlots = int64_t(1) << 26;  // batch * max_pages: at most 2^32 logits
+// Attention: pool rows (page * 64 + row) are 32-bit codes below two reserved values.
+constexpr int64_t kMaxAttPages = (int64_t(1) << 26) - 1;
 
 }  // namespace
 
@@ -33,7 +35,7 @@ const char* dsa_indexer_status_string(int status) {
     case DSA_ERR_NULL: return "a required pointer is NULL";
     case DSA_ERR_SHAPE: return "batch, max_pages, num_pages or max_c4 out of range";
     case DSA_ERR_ALIGN: return "a pointer misses its required alignment";
-    case DSA_ERR_K: return "k out of [1, max_c4]";
+    case DSA_ERR_K: return "k out of range (top-k: [1, max_c4]; attention: [1, 2048])";
     case DSA_ERR_WORKSPACE: return "workspace too small";
     case DSA_ERR_HIP: return "HIP runtime error on launch";
     default: return "unknown status";
@@ -88,6 +90,29 @@ int dsa_indexer_topk(const float* logits, const int32_t* seq_lens, int32_t batch
       misaligned16(workspace))
     return DSA_ERR_ALIGN;
   return from_hip(dsa::launch_topk(logits, seq_lens, batch, max_c4, k, out_idx, out_vals, workspace, stream));
+}
+
+size_t dsa_indexer_sparse_attention_workspace_bytes(int32_t batch, int32_t k) {
+  if (batch < 1 || batch > kMaxBatch || k < 1 || k > dsa::kMaxAttK) return 0;
+  return dsa::att_workspace_bytes(batch, k);
+}
+
+int dsa_indexer_sparse_attention(const void* q, const void* kv_pool, int64_t num_pages, const int32_t* page_table,
+                                 int32_t batch, int32_t max_pages, const int32_t* idx, int32_t k, float scale,
+                                 float* out, float* lse, void* workspace, size_t ws_bytes, hipStream_t stream) {
+  if (!q || !kv_pool || !page_table || !idx || !out || !lse) return DSA_ERR_NULL;
+  if (batch < 1 || batch > kMaxBatch || max_pages < 1 || max_pages > kMaxPages || num_pages < 1 ||
+      num_pages > kMaxAttPages)
+    return DSA_ERR_SHAPE;
+  if (k < 1 || k > dsa::kMaxAttK) return DSA_ERR_K;
+  if (!(scale == scale) || scale == __builtin_inff() || scale == -__builtin_inff()) return DSA_ERR_SHAPE;
+  const size_t need = dsa_indexer_sparse_attention_workspace_bytes(batch, k);
+  if (ws_bytes < need || (need > 0 && workspace == nullptr)) return DSA_ERR_WORKSPACE;
+  if (misaligned16(q) || misaligned16(kv_pool) || misaligned16(out) || misaligned4(lse) ||
+      misaligned4(page_table) || misaligned4(idx) || misaligned16(workspace))
+    return DSA_ERR_ALIGN;
+  return from_hip(dsa::launch_attention(q, kv_pool, num_pages, page_table, batch, max_pages, idx, k, scale, out,
+                                        lse, workspace, stream));
 }
 
 }  // extern "C"

@@ -48,4 +48,20 @@ size_t topk_workspace_words(int32_t batch, int32_t max_c4);
 hipError_t launch_topk(const float* logits, const int32_t* seq_lens, int32_t batch, int32_t max_c4,
                        int32_t k, int32_t* out_idx, float* out_vals, void* workspace, hipStream_t stream);
 
+// Sparse attention over the selected positions: 32 heads, 576-dim latents
+// (the first 512 dims are the value), at most kMaxAttK list entries per request.
+constexpr int32_t kMaxAttK = 2048;
+constexpr int kAttTargetGroups = 512;  // workgroups the split plan aims for (2 per CU)
+
+// Splits of each request's list (nsplit) and list entries per split (chunk).
+void att_plan(int32_t batch, int32_t k, int32_t* nsplit, int32_t* chunk);
+
+// Bytes of attention workspace for these sizes (0 when one split suffices).
+size_t att_workspace_bytes(int32_t batch, int32_t k);
+
+// Enqueue the attention kernel (and, with more than one split, the merge).
+hipError_t launch_attention(const void* q, const void* kv, int64_t num_pages, const int32_t* page_table,
+                            int32_t batch, int32_t max_pages, const int32_t* idx, int32_t k, float scale,
+                            float* out, float* lse, void* workspace, hipStream_t stream);
+
 }  // namespace dsa

@@ -274,3 +274,17 @@ def attention_inputs(inp: Inputs, seed: int) -> AttentionInputs:
     kv = _normal_bf16(rng, (inp.num_pages, PAGE, ATT_KD))
     return AttentionInputs(q, kv, ATT_SCALE)
 
+
+
+def random_selection(inp: Inputs, k: int, seed: int) -> np.ndarray:
+    """A selection shaped like the top-k output, int32 [B, k]: for each request
+    min(k, L) distinct positions drawn uniformly from [0, L) (L its c4 length,
+    clamped to the row width), ascending, then -1. PCG64(seed + ATT_SEED_OFFSET + 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed + ATT_SEED_OFFSET + 1))
+    out = np.full((inp.batch, k), -1, dtype=np.int32)
+    for b in range(inp.batch):
+        L = int(np.clip(inp.seq_lens[b], 0, inp.max_c4))
+        n = min(k, L)
+        if n:
+            out[b, :n] = np.sort(rng.choice(L, size=n, replace=False))
+    return out

@@ -29,13 +29,13 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 7, names
+    assert len(names) == 9, names
     for name in names:
         assert hasattr(lib, name), f"{name} not exported"
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dsa_indexer_abi_version() == 2
+    assert lib.dsa_indexer_abi_version() == 3
     for st in (OK, NULL, SHAPE, ALIGN, K, WS, -6):
         assert lib.dsa_indexer_status_string(st).decode() not in ("", "unknown status")
     assert lib.dsa_indexer_status_string(12345).decode() == "unknown status"
@@ -121,3 +121,37 @@ def test_score_fp8_shape(lib, over):
 @pytest.mark.parametrize("field,off", [("q", 8), ("k_pool_fp8", 4), ("k_scale", 2), ("logits", 4), ("page_table", 2)])
 def test_score_fp8_alignment(lib, field, off):
     assert lib.dsa_indexer_score_fp8(*score_fp8_args(**{field: A + off})) == ALIGN
+
+
+def att_args(**over):
+    args = dict(q=A, kv_pool=A, num_pages=4, page_table=A, batch=2, max_pages=3, idx=A, k=64, scale=0.1,
+                out=A, lse=A, workspace=A, ws_bytes=1 << 30, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("field", ["q", "kv_pool", "page_table", "idx", "out", "lse"])
+def test_attention_null(lib, field):
+    assert lib.dsa_indexer_sparse_attention(*att_args(**{field: None})) == NULL
+
+
+@pytest.mark.parametrize("over,want", [(dict(batch=0), SHAPE), (dict(batch=65536), SHAPE), (dict(max_pages=0), SHAPE),
+                                       (dict(max_pages=(1 << 22) + 1), SHAPE), (dict(num_pages=0), SHAPE),
+                                       (dict(num_pages=1 << 26), SHAPE), (dict(scale=float("nan")), SHAPE),
+                                       (dict(scale=float("inf")), SHAPE), (dict(k=0), K), (dict(k=2049), K),
+                                       (dict(q=A + 8), ALIGN), (dict(kv_pool=A + 2), ALIGN), (dict(out=A + 4), ALIGN),
+                                       (dict(lse=A + 2), ALIGN), (dict(idx=A + 1), ALIGN),
+                                       (dict(page_table=A + 2), ALIGN), (dict(workspace=A + 8), ALIGN)])
+def test_attention_rejects(lib, over, want):
+    assert lib.dsa_indexer_sparse_attention(*att_args(**over)) == want
+
+
+def test_attention_workspace_contract(lib):
+    # 64 requests x 2048 entries: 8 splits of 256, each 32 heads x (512 + 1) floats
+    need = lib.dsa_indexer_sparse_attention_workspace_bytes(64, 2048)
+    assert need == 64 * 8 * 32 * 513 * 4
+    assert lib.dsa_indexer_sparse_attention_workspace_bytes(600, 32) == 0  # one tile: one split
+    assert lib.dsa_indexer_sparse_attention_workspace_bytes(0, 64) == 0
+    assert lib.dsa_indexer_sparse_attention_workspace_bytes(4, 4096) == 0  # k out of range
+    assert lib.dsa_indexer_sparse_attention(*att_args(batch=64, k=2048, ws_bytes=need - 1)) == WS
+    assert lib.dsa_indexer_sparse_attention(*att_args(batch=64, k=2048, workspace=None, ws_bytes=need)) == WS

@@ -1,0 +1,178 @@
+"""GPU parity of the sparse attention over the selected positions
+(dsa_indexer_sparse_attention) against the float64 oracle.
+
+Bound per output element (derived from the arithmetic): the kernel's softmax
+weights are the exact ones times (1 + d_i), with |d_i| <= delta where delta is
+the bfloat16 rounding of the weight (unit roundoff 2^-8: 8 significant bits;
+the largest weight is not always exactly 1, since the running maximum is kept
+until a tile exceeds it by 8 in base 2), exp2's error, and the score's
+float32 summation error (at most 64 * 2^-24 * scale * sum_d |q_d k_d|, twice:
+once for the score, once for the running maximum). A weighted mean with such
+weights moves by at most delta / (1 - delta) * max_i |v_i - out|; float32
+sums of n terms add (n + 32) * 2^-24 relative. The log-sum-exp moves by at
+most delta / (1 - delta) plus the score error. A second, statistical check
+keeps the mean squared error of each request within 4 * 2^-16 times the
+variance that the weight rounding predicts (12x what uniform rounding errors
+give), which catches a dropped or doubled position that the bound alone
+would let through.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from sparse_attention_kv_indexer_amd import workloads as wl
+
+from gpu_helpers import say
+
+pytestmark = pytest.mark.gpu
+
+U = 2.0 ** -8  # bfloat16 unit roundoff
+VD = wl.ATT_VD
+UNWRITTEN = 1.0e30
+
+
+def run_attention(lib, page_table, att, idx, scale, device="cuda"):
+    import torch
+
+    t = lib.attention_to_device(att, device)
+    B, k = idx.shape
+    pt = torch.from_numpy(np.ascontiguousarray(page_table, dtype=np.int32)).to(device)
+    ix = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).to(device)
+    out = torch.full((B, wl.ATT_HEADS, VD), UNWRITTEN, dtype=torch.float32, device=device)
+    lse = torch.full((B, wl.ATT_HEADS), UNWRITTEN, dtype=torch.float32, device=device)
+    lib.sparse_attention(t["q"], t["kv_pool"], pt, ix, scale, out=out, lse=lse)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().astype(np.float64), lse.cpu().numpy().astype(np.float64)
+
+
+def check_attention(got_o, got_l, page_table, att, idx, scale, stat=True):
+    ref_o, ref_l = oracle.sparse_attention(att.q_bits, att.kv_bits, page_table, idx, scale, VD)
+    assert not np.any(got_o == UNWRITTEN) and not np.any(got_l == UNWRITTEN), "unwritten output"
+    q = oracle.bf16_bits_to_f64(att.q_bits)
+    B = idx.shape[0]
+    worst = 0.0
+    for b in range(B):
+        if np.isnan(ref_l[b, 0]):
+            assert np.all(np.isnan(got_o[b])) and np.all(np.isnan(got_l[b])), f"request {b} should be NaN"
+            continue
+        if np.isneginf(ref_l[b, 0]):
+            assert np.all(got_o[b] == 0) and np.all(np.isneginf(got_l[b])), f"request {b} should be empty"
+            continue
+        pos = np.asarray([int(s) for s in idx[b] if s >= 0], dtype=np.int64)
+        pages = np.asarray(page_table[b], dtype=np.int64)[pos // wl.PAGE]
+        lat = oracle.bf16_bits_to_f64(att.kv_bits[pages, pos % wl.PAGE])  # [n, 576]
+        n = pos.size
+        A = abs(scale) * (np.abs(q[b]) @ np.abs(lat).T)  # [H, n] score magnitudes
+        eps_s = 64 * 2.0 ** -24 * A.max(axis=1)  # [H]
+        delta = U + 2.0 ** -20 + 2 * eps_s
+        rel = delta / (1 - delta)
+        acc = (n + 32) * 2.0 ** -24
+        v = lat[:, :VD]
+        O = ref_o[b]
+        spread = np.maximum(v.max(axis=0)[None, :] - O, O - v.min(axis=0)[None, :])  # max_i |v_i - O|, [H, VD]
+        tol_o = rel[:, None] * spread + acc * np.abs(v).max(axis=0)[None, :] + 1e-30
+        err_o = np.abs(got_o[b] - ref_o[b])
+        assert np.all(err_o <= tol_o), (
+            f"request {b}: out error {err_o.max():.3e} above bound at {np.unravel_index(np.argmax(err_o - tol_o), err_o.shape)}")
+        tol_l = rel + eps_s + acc + 2.0 ** -22 * np.abs(ref_l[b])
+        err_l = np.abs(got_l[b] - ref_l[b])
+        assert np.all(err_l <= tol_l), f"request {b}: lse error {err_l.max():.3e} above bound"
+        if stat:
+            s = scale * (q[b] @ lat.T)
+            w = np.exp(s - s.max(axis=1, keepdims=True))
+            w /= w.sum(axis=1, keepdims=True)  # [H, n]
+            w2 = w * w
+            E = w2 @ (v * v) - 2 * O * (w2 @ v) + O * O * w2.sum(axis=1, keepdims=True)  # sum_i w_i^2 (v_i - O)^2
+            mse = np.mean(err_o ** 2)
+            assert mse <= 4 * U * U * np.mean(E) + 1e-18, f"request {b}: mse {mse:.3e} vs {4 * U * U * np.mean(E):.3e}"
+        worst = max(worst, float((err_o / tol_o).max()))
+    return worst
+
+
+def _case(name, k=None, seed=0):
+    inp = wl.generate(name)
+    att = wl.attention_inputs(inp, seed)
+    idx = wl.random_selection(inp, k or inp.topk, seed)
+    return inp, att, idx
+
+
+@pytest.mark.parametrize("name", ["tiny", "c2", "c3"])
+def test_workload_parity(lib, name):
+    inp, att, idx = _case(name)
+    say(f"attention {name} B={inp.batch} k={idx.shape[1]} pages={inp.num_pages}")
+    o, l = run_attention(lib, inp.page_table, att, idx, wl.ATT_SCALE)
+    worst = check_attention(o, l, inp.page_table, att, idx, wl.ATT_SCALE)
+    say(f"attention {name}: worst error / bound {worst:.3f}")
+
+
+def test_one_split_per_request(lib):
+    """600 requests: one split each, written without the merge; ragged last tile (k = 100)."""
+    inp = wl.random_case(11, 600, 3)
+    att = wl.attention_inputs(inp, 11)
+    idx = wl.random_selection(inp, 100, 11)
+    say(f"attention one split B=600 k=100")
+    assert lib.sparse_attention_workspace_bytes(600, 100) == 0
+    o, l = run_attention(lib, inp.page_table, att, idx, wl.ATT_SCALE)
+    check_attention(o, l, inp.page_table, att, idx, wl.ATT_SCALE)
+
+
+def test_many_splits_one_request(lib):
+    """One request of 2048 entries: 64 splits of one tile, merged."""
+    inp = wl.random_case(12, 1, 80, lens=[80 * 64])
+    att = wl.attention_inputs(inp, 12)
+    idx = wl.random_selection(inp, 2048, 12)
+    say("attention B=1 k=2048 (64 splits)")
+    o, l = run_attention(lib, inp.page_table, att, idx, wl.ATT_SCALE)
+    check_attention(o, l, inp.page_table, att, idx, wl.ATT_SCALE)
+
+
+def test_edge_rows(lib):
+    """Empty, scattered -1, duplicated, single-entry, off-table and off-pool
+    requests side by side, over three splits (k = 70)."""
+    inp = wl.random_case(13, 9, 6, lens=[384, 384, 300, 384, 1, 200, 384, 384, 70])
+    att = wl.attention_inputs(inp, 13)
+    idx = wl.random_selection(inp, 70, 13)
+    pt = inp.page_table.copy()
+    idx[0] = -1                                   # nothing selected
+    idx[1, 5:60:3] = -1                           # holes in the middle
+    idx[2, 10:20] = idx[2, 0]                     # one position ten more times
+    idx[3, 1:] = -1                               # a single entry, two empty splits
+    idx[5, 40] = pt.shape[1] * 64                 # past the page table
+    pt[6, idx[6, 33] // 64] = inp.num_pages + 7   # a page outside the pool
+    idx[7, :] = idx[7, ::-1].copy()               # descending order, -1 first
+    say("attention edge rows B=9 k=70")
+    o, l = run_attention(lib, pt, att, idx, wl.ATT_SCALE)
+    check_attention(o, l, pt, att, idx, wl.ATT_SCALE)
+    assert np.all(np.isnan(o[5])) and np.all(np.isnan(o[6])) and np.all(np.isfinite(o[[1, 2, 3, 4, 7, 8]]))
+
+
+def test_peaked_softmax_rescales(lib):
+    """A large scale: near one-hot weights and a running maximum that grows by
+    more than the rescale headroom on many tiles."""
+    inp, att, idx = _case("c2", seed=3)
+    say("attention c2 scale=2")
+    o, l = run_attention(lib, inp.page_table, att, idx, 2.0)
+    check_attention(o, l, inp.page_table, att, idx, 2.0)
+
+
+def test_zero_scale_is_the_exact_mean(lib):
+    """scale = 0: every weight is exactly 1, so the output is the mean of the
+    selected values up to float32 summation, and lse = log(n)."""
+    inp, att, idx = _case("c2", seed=4)
+    say("attention c2 scale=0")
+    o, l = run_attention(lib, inp.page_table, att, idx, 0.0)
+    for b in range(inp.batch):
+        pos = idx[b][idx[b] >= 0].astype(np.int64)
+        lat = oracle.bf16_bits_to_f64(att.kv_bits[inp.page_table[b][pos // 64], pos % 64])[:, :VD]
+        mean = lat.mean(axis=0)
+        tol = (pos.size + 32) * 2.0 ** -24 * np.abs(lat).mean(axis=0) + 2.0 ** -23 * np.abs(mean)
+        assert np.all(np.abs(o[b] - mean[None, :]) <= tol[None, :]), f"request {b}"
+        assert np.allclose(l[b], np.log(pos.size), rtol=0, atol=4e-6)
+
+
+def test_repeatable(lib):
+    inp, att, idx = _case("c2", seed=5)
+    say("attention c2 twice")
+    a = run_attention(lib, inp.page_table, att, idx, wl.ATT_SCALE)
+    b = run_attention(lib, inp.page_table, att, idx, wl.ATT_SCALE)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])

@@ -114,3 +114,14 @@ def test_positions_off_the_table_or_pool_poison_only_their_request():
     idx2[0, 0] = -7
     out2, _ = oracle.sparse_attention(q, kv, inp.page_table, idx2, 0.5, 8)
     assert np.all(np.isfinite(out2[0]))
+
+
+def test_selection_recipe():
+    inp = wl.random_case(7, 5, 4, lens=[0, 10, 64, 256, 300])
+    sel = wl.random_selection(inp, 100, 0)
+    assert sel.dtype == np.int32 and sel.shape == (5, 100)
+    for b, L in enumerate([0, 10, 64, 256, 256]):
+        n = min(100, L)
+        row = sel[b]
+        assert np.all(row[n:] == -1)
+        assert np.all(np.diff(row[:n]) > 0) and (n == 0 or (row[0] >= 0 and row[n - 1] < L))
