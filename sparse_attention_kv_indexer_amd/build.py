@@ -29,6 +29,9 @@ FLAGS = [
     "-Wall",
     # no packed-fp32 instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results in ordinary VGPRs: keeps loop-carried accumulators out of
+    # AGPRs (which would be copied in and out on every iteration)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
 ]
 
 

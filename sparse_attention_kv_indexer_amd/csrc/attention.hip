@@ -9,23 +9,25 @@
 //
 // attention_kernel: one 256-thread workgroup per (request, split), where a
 // split is a run of at most `chunk` entries of the request's list. It
-// processes tiles of 32 positions:
-//   - the 32 latents are staged into LDS: each thread copies 144 B of one row
-//     with 16-byte loads, and each wave's loads cover 8 rows of 128 B lines
-//     per instruction. The next tile's loads are issued while the current
-//     tile is being computed;
-//   - S^T = K Q^T (32 positions x 32 heads) uses v_mfma_f32_32x32x16_bf16,
-//     with the 576-dim contraction split over the 4 waves (9 k-steps each,
-//     that wave's queries held in registers). The 4 partial tiles are summed
-//     through LDS, and every wave then holds the whole S^T tile in the MFMA
-//     result layout (one head per lane, 16 of the 32 positions per lane);
-//   - online softmax in base 2. Per head, the running maximum is kept unless
-//     a tile's maximum exceeds it by more than 8, so the output is rescaled
-//     only when the maximum grows by that much (exact either way, because
-//     the output and the sum of weights share the reference point);
-//   - O^T += V^T P^T with the same MFMA: each wave owns 128 of the 512 value
-//     dims. The weights P already sit in the B-operand layout, and V^T is
-//     read from LDS with 16-bit reads.
+// processes tiles of 32 positions, double-buffered in LDS:
+//   - staging: each thread copies 144 B of one latent row with 16-byte loads
+//     (a wave's load covers 8 rows of 128 B lines), issued one tile ahead and
+//     written to the LDS buffer the previous tile has released. Rows are
+//     stored as 72 chunks of 16 B, with chunk c of row r at c ^ swz(r), which
+//     keeps every LDS access pattern below free of bank conflicts;
+//   - wave (hh, dh) owns heads 16hh..16hh+15 and value dims 256dh..256dh+255.
+//     It computes S^T for all 32 tile positions of its heads over the 576
+//     dims with v_mfma_f32_16x16x32_bf16 (its queries held in registers; the
+//     two waves of a head half compute the same scores), so its softmax needs
+//     nothing from other waves;
+//   - online softmax in base 2, per wave: the output is rescaled only when a
+//     head's maximum grows by more than 8 (exact either way, as the output
+//     and the sum of weights share the reference). The weights, rounded to
+//     bf16, sit in the registers in the B-operand layout of the value product;
+//   - O^T += V^T P^T, again on 16x16x32 blocks: V^T comes straight from the
+//     staged rows through ds_read_b64_tr_b16 (each 16-lane group reads a
+//     4 x 16 block of bf16 and receives it transposed).
+// One barrier per tile: the staged buffer of the next tile is complete.
 // With one split the kernel writes the normalised output and the log-sum-exp
 // directly. Otherwise it writes each split's normalised partial output and
 // log-sum-exp to the workspace, and merge_kernel combines them.
@@ -41,25 +43,29 @@ namespace {
 constexpr int kAttHeads = 32;
 constexpr int kKD = 576;
 constexpr int kVD = 512;
-constexpr int kLatBytes = kKD * 2;             // one latent: 1152 B
-constexpr int kLdsRow = kLatBytes + 16;        // padded LDS row: conflict-free row-wise and column-wise reads
+constexpr int kLatBytes = kKD * 2;             // one latent: 1152 B = 72 chunks of 16 B
 constexpr int kTile = 32;                      // positions per tile
+constexpr int kTileBytes = kTile * kLatBytes;  // 36 KiB
+constexpr int kBufs = 4;                       // staged tiles: one computed, three loading
+constexpr int kSRow = 36;                      // floats per row (head) of the score tile: 32 + padding
 constexpr int kAttThreads = 256;
 constexpr int kAttWaves = kAttThreads / 64;
-constexpr int kQSteps = kKD / 16 / kAttWaves;  // 9 MFMA k-steps per wave
+constexpr int kQSteps = kKD / 32;              // 18 k-steps of the 16x16x32 MFMA
 constexpr int kStage = kLatBytes / 128;        // 9 loads of 16 B per thread per tile
-constexpr int kDimsPerWave = kVD / kAttWaves;  // 128 value dims per wave
 constexpr int kMergeThreads = 256;
 constexpr int kMergeParts = kAttHeads * kVD / 4 / kMergeThreads;  // 16 workgroups per request
 constexpr uint32_t kSkip = 0xFFFFFFFFu;        // row code: list entry not attended
 constexpr uint32_t kBad = 0xFFFFFFFEu;         // row code: entry past the table or on a page outside the pool
-constexpr float kRegrow = 8.0f;                // log2 headroom before the output is rescaled
+constexpr float kRegrow = 8.0f;                // log2 headroom of the weights over the running maximum
 constexpr float kLn2 = 0.693147180559945309f;
 
 static_assert(kStage * 128 == kLatBytes, "a row is 8 threads x kStage x 16 B");
 static_assert(kTile * 8 == kAttThreads, "8 threads stage each row of a tile");
+static_assert(kMaxAttChunk % kTile == 0, "splits are whole tiles");
 
-typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((__vector_size__(4 * sizeof(__bf16))));
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
 struct AttArgs {
   const uint16_t* q;          // [batch][32][576] bf16
@@ -84,7 +90,31 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
                                                  c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
+                                                 c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float xor_lanes(float v, int m) { return __shfl_xor(v, m, 64); }
+
+// Chunk c of staged row r sits at chunk c ^ swz(r) of that row. Over any 16
+// aligned rows, swz takes each value once on the even and once on the odd
+// rows and once on each aligned 8; swz >> 1 differs on any aligned 4 rows.
+// So reads of one chunk from 16 rows (scores) and of 32 B from 4 or 8 rows
+// (the transposed value reads) never share a bank, whether the LDS serves
+// 128 or 256 bytes per clock.
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) ^ (3 * ((r >> 2) & 1)) ^ ((r >> 3) & 1); }
+
+// 4 bf16 of LDS, transposed across each 16-lane group.
+__device__ __forceinline__ u32x2 read_tr(const unsigned char* p) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(p)));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b, float& sum) {
+  const __bf16 x = (__bf16)a, y = (__bf16)b;
+  sum += (float)x + (float)y;
+  return (uint32_t)__builtin_bit_cast(uint16_t, x) | ((uint32_t)__builtin_bit_cast(uint16_t, y) << 16);
+}
 
 // Request and split of this workgroup: workgroup i runs on XCD i % 8, so
 // request b is handled by workgroups with i % 8 == b % 8.
@@ -95,19 +125,57 @@ __device__ __forceinline__ void att_place(int nsplit, int& b, int& s) {
   s = slot % nsplit;
 }
 
-__global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+// Direct-to-LDS load of 16 B per lane: lane l's bytes land at lds + 16 l
+// (lds is a wave-uniform LDS byte address). Issued as inline assembly so that the compiler does
+// not track it: its completion is awaited explicitly (s_waitcnt vmcnt, then a
+// barrier) before any wave reads the buffer. Extra outstanding loads can only
+// make the compiler's own vmcnt waits stricter, never looser.
+__device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(lds)
+      : "memory");
+}
+
+// Encoding of s_waitcnt that waits until at most n vector-memory operations
+// and no LDS operations of this wave are outstanding.
+constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8); }
+constexpr int kLgkmWait = vm_lgkm_wait(63);  // LDS only
+
+// Workgroup barrier after this wave's LDS accesses have completed (a bare
+// s_barrier does not wait for them).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kLgkmWait);
+  __builtin_amdgcn_s_barrier();
+}
+
+__global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attention_kernel(const AttArgs a) {
-  __shared__ __attribute__((aligned(16))) unsigned char tile[kTile * kLdsRow];
-  __shared__ f32x4 spart[kAttWaves * 4 * 64];
-  __shared__ uint32_t rows[kMaxAttK];
+  // Tile t is staged in buffer t % 4 while tiles t+1 .. t+3 are loading.
+  __shared__ __attribute__((aligned(16))) unsigned char tbuf[kBufs * kTileBytes];
+  __shared__ __attribute__((aligned(16))) float sbuf[kAttHeads * kSRow];
+  __shared__ float mbuf[2][kAttHeads];
+  __shared__ uint32_t rows[kMaxAttChunk];
 
   int b, s;
   att_place(a.nsplit, b, s);
   if (b >= a.batch) return;
-  const int tid = (int)threadIdx.x, lane = tid & 63, wv = tid >> 6, hf = lane >> 5, l32 = lane & 31;
+  const int tid = (int)threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g0 = s * a.chunk;
   const int n = min(a.chunk, a.k - g0);  // list entries of this split, >= 1
   const int ntiles = (n + kTile - 1) / kTile;
+
+  // Wave (hh, dh): heads 16hh..16hh+15, value dims 256dh..256dh+255.
+  // Lane (g, j): column/row j of every 16x16 block, k-slots 8g..8g+7.
+  const int g = lane >> 4, j = lane & 15;
+  const rsrc_t qr = make_rsrc(a.q + (int64_t)b * kAttHeads * kKD, kAttHeads * kLatBytes);
+  u32x4 qv[kQSteps];  // queries of head 16(wv >> 1) + j, k-slots 8g.. of each 32-dim step
+#pragma unroll
+  for (int st = 0; st < kQSteps; ++st)
+    qv[st] = __builtin_amdgcn_raw_buffer_load_b128(qr, (16 * (wv >> 1) + j) * kLatBytes + (4 * st + g) * 16, 0, 0);
 
   // Resolve every entry of the split to a pool row (page * 64 + slot row).
   const rsrc_t ir = make_rsrc(a.idx + (int64_t)b * a.k, (uint32_t)a.k * 4u);
@@ -128,115 +196,159 @@ void attention_kernel(const AttArgs a) {
     bad |= v == kBad;
     rows[u] = v;
   }
-
-  // This wave's slice of the queries: B operand of k-steps 9*wv .. 9*wv+8.
-  const rsrc_t qr = make_rsrc(a.q + (int64_t)b * kAttHeads * kKD, kAttHeads * kLatBytes);
-  u32x4 qv[kQSteps];
-#pragma unroll
-  for (int j = 0; j < kQSteps; ++j)
-    qv[j] = __builtin_amdgcn_raw_buffer_load_b128(qr, l32 * kLatBytes + (2 * (kQSteps * wv + j) + hf) * 16, 0, 0);
-
   bad = __syncthreads_or(bad);  // also publishes rows[]
 
-  // Staging: thread tid copies bytes [16*(tid%8) + 128*i, +16) of tile row tid/8.
-  const int srow = tid >> 3, scol = (tid & 7) * 16;
-  u32x4 R[kStage];
-  auto stage_load = [&](int t) {
-    const uint32_t v = rows[t * kTile + srow];
-    const uint64_t row = v >= kBad ? 0u : v;  // skipped and bad entries read row 0 (never used)
-    const unsigned char* src = reinterpret_cast<const unsigned char*>(a.kv) + row * kLatBytes + scol;
+  // Staging with direct-to-LDS loads: wave wv's load i fills LDS chunks
+  // 64(9wv + i) .. +63 of the tile (lane -> +lane). LDS chunk L is row L / 72,
+  // stored position L % 72, which holds row chunk (L % 72) ^ swz(row).
+  int drow[kStage], dsrc[kStage];
 #pragma unroll
-    for (int i = 0; i < kStage; ++i)
-      R[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + 128 * i));
+  for (int i = 0; i < kStage; ++i) {
+    const int L = 64 * (kStage * wv + i) + lane;
+    const int r = L / 72, p = L % 72;
+    drow[i] = r;
+    dsrc[i] = ((p & ~7) | ((p & 7) ^ swz(r))) * 16;
+  }
+  const unsigned char* kvb = reinterpret_cast<const unsigned char*>(a.kv);
+  const uint32_t lds_tiles =
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)tbuf + 1024u * kStage * wv;
+  auto stage = [&](int buf, int t) {
+    uint32_t v[kStage];
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) v[i] = rows[t * kTile + drow[i]];
+#pragma unroll
+    for (int i = 0; i < kStage; ++i) {
+      const uint64_t row = v[i] >= kBad ? 0u : v[i];  // skipped and bad entries read row 0 (never used)
+      dma16(kvb + row * kLatBytes + dsrc[i],
+            __builtin_amdgcn_readfirstlane(lds_tiles + (uint32_t)(buf * kTileBytes + 1024 * i)));
+    }
   };
-  stage_load(0);
 
-  f32x16 O[4];
-#pragma unroll
-  for (int t4 = 0; t4 < 4; ++t4)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) O[t4][r] = 0.f;
-  float m_run = -__builtin_inff(), l_run = 0.f;
+  // Scores: wave (ph, hh) computes S^T for tile positions 16ph..16ph+15 and
+  // heads 16hh..16hh+15 over the 576 dims (v_mfma_f32_16x16x32_bf16, lane
+  // (g, j): row/column j, k-slots 8g..8g+7). It publishes the block and its
+  // per-head maximum; after a barrier every wave reads back the whole 32 x 32
+  // tile and runs the same softmax, so no other agreement is needed.
+  const int ph = wv & 1, hh = wv >> 1;
+  const int kofs_even = (16 * ph + j) * kLatBytes + ((g ^ swz(j)) * 16);
+  const int kofs_odd = (16 * ph + j) * kLatBytes + (((4 + g) ^ swz(j)) * 16);
+  const int s_wr = (16 * hh + j) * kSRow + 16 * ph + 4 * g;  // floats into sbuf
 
-  const unsigned char* kbase = tile + l32 * kLdsRow + hf * 16 + kQSteps * wv * 32;
-  const unsigned char* vbase = tile + 4 * hf * kLdsRow + 2 * l32 + 2 * kDimsPerWave * wv;
-  unsigned char* sdst = tile + srow * kLdsRow + scol;
-
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // every wave is done with the previous tile's LDS
+  // Values: wave wv owns dims 128wv..128wv+127 for all 32 heads: O^T blocks
+  // (16 dims x 16 heads) for dim block db and head block hb. A = V^T via
+  // ds_read_b64_tr_b16: lane (g, kk, aa) reads tile row 8g + 4ld + kk at dims
+  // d0 + 4aa .. +3 of block d0 = 128wv + 16db; B = P^T: k-slot (g, i) is tile
+  // position 8g + i.
+  const int kk = (lane & 15) >> 2, aa = lane & 3;
+  int vb[2];  // [ld]: tile row 8g + 4ld + kk, dims of block 0 (swizzle applied per block below)
+  int vx[2][4];
 #pragma unroll
-    for (int i = 0; i < kStage; ++i) *reinterpret_cast<u32x4*>(sdst + 128 * i) = R[i];
-    __syncthreads();
-    if (t + 1 < ntiles) stage_load(t + 1);
-
-    // Partial S^T over this wave's 144 dims.
-    f32x16 S;
+  for (int ld = 0; ld < 2; ++ld) {
+    const int r = 8 * g + 4 * ld + kk;
+    vb[ld] = r * kLatBytes + 16 * (16 * wv) + 8 * (aa & 1);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) S[r] = 0.f;
-#pragma unroll
-    for (int j = 0; j < kQSteps; ++j) S = mfma(*reinterpret_cast<const u32x4*>(kbase + 32 * j), qv[j], S);
-#pragma unroll
-    for (int g = 0; g < 4; ++g) spart[(wv * 4 + g) * 64 + lane] = f32x4{S[4 * g], S[4 * g + 1], S[4 * g + 2], S[4 * g + 3]};
-    const uint32_t mask = (uint32_t)__ballot(rows[t * kTile + l32] < kBad);
-    __syncthreads();
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      f32x4 v = spart[g * 64 + lane];
-#pragma unroll
-      for (int w2 = 1; w2 < kAttWaves; ++w2) v += spart[(w2 * 4 + g) * 64 + lane];
-      S[4 * g] = v[0], S[4 * g + 1] = v[1], S[4 * g + 2] = v[2], S[4 * g + 3] = v[3];
-    }
-
-    // Lane (head l32, half hf) register r holds tile position 8(r/4) + 4hf + r%4.
-    const uint32_t ml = mask >> (4 * hf);
-    float mt = -__builtin_inff();
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      S[r] = ((ml >> (8 * (r >> 2) + (r & 3))) & 1u) ? S[r] * a.c : -__builtin_inff();
-      mt = fmaxf(mt, S[r]);
-    }
-    mt = fmaxf(mt, xor32(mt));
-    if (__any(mt > m_run + kRegrow)) {
-      const float mn = fmaxf(m_run, mt);
-      const float alpha = m_run == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run - mn);
-#pragma unroll
-      for (int t4 = 0; t4 < 4; ++t4) O[t4] *= alpha;
-      l_run *= alpha;
-      m_run = mn;
-    }
-    const float ref = m_run == -__builtin_inff() ? 0.f : m_run;
-    u32x4 P[2];
-    float lsum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const __bf16 p0 = (__bf16)__builtin_amdgcn_exp2f(S[r] - ref);
-      const __bf16 p1 = (__bf16)__builtin_amdgcn_exp2f(S[r + 1] - ref);
-      lsum += (float)p0 + (float)p1;
-      P[r >> 3][(r >> 1) & 3] = (uint32_t)__builtin_bit_cast(uint16_t, p0) |
-                                ((uint32_t)__builtin_bit_cast(uint16_t, p1) << 16);
-    }
-    l_run += lsum;
-
-    // O^T[dims of this wave] += V^T P^T; k-slot (hf, i) of step js is tile
-    // position 16js + 8(i/4) + 4hf + i%4, matching P's layout.
-#pragma unroll
-    for (int t4 = 0; t4 < 4; ++t4) {
-#pragma unroll
-      for (int js = 0; js < 2; ++js) {
-        u16x8 e;
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-          e[i] = *reinterpret_cast<const uint16_t*>(vbase + (16 * js + 8 * (i >> 2) + (i & 3)) * kLdsRow + 64 * t4);
-        O[t4] = mfma(__builtin_bit_cast(u32x4, e), P[js], O[t4]);
-      }
-    }
+    for (int m4 = 0; m4 < 4; ++m4) vx[ld][m4] = ((2 * m4 + (aa >> 1)) ^ swz(r)) * 16;
   }
 
-  // Finish: sum of weights over both halves, normalise, log-sum-exp (natural log).
-  const float l_tot = l_run + xor32(l_run);
-  float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  float lse_v = l_tot > 0.f ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -__builtin_inff();
-  if (bad) inv = lse_v = __builtin_nanf("");
+  f32x4 O[2][8];  // [hb][db]: dims 128wv + 16db + 4g + r, head 16hb + j
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+    for (int db = 0; db < 8; ++db) O[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run[2] = {-__builtin_inff(), -__builtin_inff()}, l_run[2] = {0.f, 0.f};
+
+  auto compute = [&](const unsigned char* cur, int t) {
+    f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = S0;
+    {
+      u32x4 kx[kQSteps];
+#pragma unroll
+      for (int st = 0; st < kQSteps; ++st)
+        kx[st] = *reinterpret_cast<const u32x4*>(cur + ((st & 1) ? kofs_odd : kofs_even) + 64 * (st & ~1));
+#pragma unroll
+      for (int st = 0; st < kQSteps; st += 2) {
+        S0 = mfma16(kx[st], qv[st], S0);
+        S1 = mfma16(kx[st + 1], qv[st + 1], S1);
+      }
+    }
+    // Register r: tile position 16ph + 4g + r, head 16hh + j.
+    const uint32_t mask = (uint32_t)__ballot(rows[t * kTile + (lane & 31)] < kBad);
+    f32x4 S = S0 + S1;
+    const uint32_t mine = mask >> (16 * ph + 4 * g);
+    float mt = -__builtin_inff();
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      S[r] = ((mine >> r) & 1u) ? S[r] * a.c : -__builtin_inff();
+      mt = fmaxf(mt, S[r]);
+    }
+    mt = fmaxf(mt, xor_lanes(mt, 16));
+    mt = fmaxf(mt, xor_lanes(mt, 32));
+    *reinterpret_cast<f32x4*>(sbuf + s_wr) = S;
+    if (g == 0) mbuf[ph][16 * hh + j] = mt;
+    lds_barrier();
+
+    // Softmax over the tile for heads j (hb = 0) and 16 + j (hb = 1): this
+    // lane's positions 8g..8g+7.
+    u32x4 P[2];
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb) {
+      const int h = 16 * hb + j;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(sbuf + h * kSRow + 8 * g);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(sbuf + h * kSRow + 8 * g + 4);
+      const float tm = fmaxf(mbuf[0][h], mbuf[1][h]);
+      if (__any(tm > m_run[hb] + kRegrow)) {
+        const float mn = fmaxf(m_run[hb], tm);
+        const float alpha = m_run[hb] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run[hb] - mn);
+#pragma unroll
+        for (int db = 0; db < 8; ++db) O[hb][db] *= alpha;
+        l_run[hb] *= alpha;
+        m_run[hb] = mn;
+      }
+      const float ref = m_run[hb] == -__builtin_inff() ? 0.f : m_run[hb];
+      P[hb][0] = pack_bf16(__builtin_amdgcn_exp2f(x0[0] - ref), __builtin_amdgcn_exp2f(x0[1] - ref), l_run[hb]);
+      P[hb][1] = pack_bf16(__builtin_amdgcn_exp2f(x0[2] - ref), __builtin_amdgcn_exp2f(x0[3] - ref), l_run[hb]);
+      P[hb][2] = pack_bf16(__builtin_amdgcn_exp2f(x1[0] - ref), __builtin_amdgcn_exp2f(x1[1] - ref), l_run[hb]);
+      P[hb][3] = pack_bf16(__builtin_amdgcn_exp2f(x1[2] - ref), __builtin_amdgcn_exp2f(x1[3] - ref), l_run[hb]);
+    }
+
+    // O^T += V^T P^T: each V^T block feeds both head blocks.
+    u32x4 va[8];
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      const u32x2 lo = read_tr(cur + vb[0] + 128 * (db >> 2) + vx[0][db & 3]);
+      const u32x2 hi = read_tr(cur + vb[1] + 128 * (db >> 2) + vx[1][db & 3]);
+      va[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+#pragma unroll
+    for (int db = 0; db < 8; ++db) {
+      O[0][db] = mfma16(va[db], P[0], O[0][db]);
+      O[1][db] = mfma16(va[db], P[1], O[1][db]);
+    }
+  };
+
+  // Tile t: wait for this wave's loads of it (those of tiles t+1, t+2 may
+  // still be in flight) and for its LDS accesses, barrier (everyone's loads
+  // of tile t have landed, and everyone is done with tile t-1), refill tile
+  // t-1's buffer with tile t+3, compute tile t.
+  __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));  // the queries have landed; only tile loads are outstanding below
+  for (int t = 0; t < kBufs - 1 && t < ntiles; ++t) stage(t, t);
+  for (int t = 0; t < ntiles; ++t) {
+    if (t + 2 < ntiles)
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * kStage));
+    else if (t + 1 < ntiles)
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(kStage));
+    else
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+    __builtin_amdgcn_s_barrier();
+    if (t + 3 < ntiles) stage((t + 3) & (kBufs - 1), t + 3);
+    compute(tbuf + (t & (kBufs - 1)) * kTileBytes, t);
+  }
+
+  // Sums of weights of this lane's two heads over all lanes (g) of the wave.
+#pragma unroll
+  for (int hb = 0; hb < 2; ++hb) {
+    l_run[hb] += xor_lanes(l_run[hb], 16);
+    l_run[hb] += xor_lanes(l_run[hb], 32);
+  }
   float* dst_o;
   float* dst_l;
   if (a.nsplit == 1) {
@@ -248,17 +360,21 @@ void attention_kernel(const AttArgs a) {
     dst_l = a.part_lse + part * kAttHeads;
   }
   const rsrc_t orr = make_rsrc(dst_o, kAttHeads * kVD * 4);
+  const rsrc_t lr = make_rsrc(dst_l, kAttHeads * 4);
 #pragma unroll
-  for (int t4 = 0; t4 < 4; ++t4)
+  for (int hb = 0; hb < 2; ++hb) {
+    const int h = 16 * hb + j;
+    const float inv = bad ? __builtin_nanf("") : (l_run[hb] > 0.f ? 1.0f / l_run[hb] : 0.f);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const f32x4 v = f32x4{O[t4][4 * g], O[t4][4 * g + 1], O[t4][4 * g + 2], O[t4][4 * g + 3]} * inv;
-      const int d = kDimsPerWave * wv + 32 * t4 + 8 * g + 4 * hf;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), orr, (l32 * kVD + d) * 4, 0, 0);
+    for (int db = 0; db < 8; ++db) {
+      const int d = 128 * wv + 16 * db + 4 * g;
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, O[hb][db] * inv), orr, (h * kVD + d) * 4, 0, 0);
     }
-  if (wv == 0 && hf == 0) {
-    const rsrc_t lr = make_rsrc(dst_l, kAttHeads * 4);
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_v), lr, l32 * 4, 0, 0);
+    if (wv == 0 && g == 0) {
+      float lse_v = l_run[hb] > 0.f ? (m_run[hb] + __builtin_amdgcn_logf(l_run[hb])) * kLn2 : -__builtin_inff();
+      if (bad) lse_v = __builtin_nanf("");
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_v), lr, h * 4, 0, 0);
+    }
   }
 }
 
@@ -312,7 +428,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const AttArgs a) {
 
 void att_plan(int32_t batch, int32_t k, int32_t* nsplit, int32_t* chunk) {
   const int tiles = (k + kTile - 1) / kTile;
-  const int want = max(1, min(tiles, (kAttTargetGroups + batch - 1) / batch));
+  const int want = max((tiles * kTile + kMaxAttChunk - 1) / kMaxAttChunk,
+                       max(1, min(tiles, (kAttTargetGroups + batch - 1) / batch)));
   const int per = (tiles + want - 1) / want;
   *chunk = per * kTile;
   *nsplit = (tiles + per - 1) / per;

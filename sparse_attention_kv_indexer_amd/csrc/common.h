@@ -51,7 +51,8 @@ hipError_t launch_topk(const float* logits, const int32_t* seq_lens, int32_t bat
 // Sparse attention over the selected positions: 32 heads, 576-dim latents
 // (the first 512 dims are the value), at most kMaxAttK list entries per request.
 constexpr int32_t kMaxAttK = 2048;
-constexpr int kAttTargetGroups = 512;  // workgroups the split plan aims for (2 per CU)
+constexpr int32_t kMaxAttChunk = 1024;  // list entries one workgroup handles at most
+constexpr int kAttTargetGroups = 256;  // workgroups the split plan aims for (one per CU)
 
 // Splits of each request's list (nsplit) and list entries per split (chunk).
 void att_plan(int32_t batch, int32_t k, int32_t* nsplit, int32_t* chunk);

@@ -147,10 +147,12 @@ def test_attention_rejects(lib, over, want):
 
 
 def test_attention_workspace_contract(lib):
-    # 64 requests x 2048 entries: 8 splits of 256, each 32 heads x (512 + 1) floats
+    # 64 requests x 2048 entries: 4 splits of 512, each 32 heads x (512 + 1) floats
     need = lib.dsa_indexer_sparse_attention_workspace_bytes(64, 2048)
-    assert need == 64 * 8 * 32 * 513 * 4
+    assert need == 64 * 4 * 32 * 513 * 4
     assert lib.dsa_indexer_sparse_attention_workspace_bytes(600, 32) == 0  # one tile: one split
+    assert lib.dsa_indexer_sparse_attention_workspace_bytes(600, 1024) == 0  # 1024 entries fit one split
+    assert lib.dsa_indexer_sparse_attention_workspace_bytes(600, 1025) == 600 * 2 * 32 * 513 * 4
     assert lib.dsa_indexer_sparse_attention_workspace_bytes(0, 64) == 0
     assert lib.dsa_indexer_sparse_attention_workspace_bytes(4, 4096) == 0  # k out of range
     assert lib.dsa_indexer_sparse_attention(*att_args(batch=64, k=2048, ws_bytes=need - 1)) == WS
