@@ -53,25 +53,29 @@ def parse():
     return ap.parse_args()
 
 
-def source_digest() -> str:
+ATT_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attention_kernel_traffic.txt")
+ATT_SOURCES = ["sparse_attention_kv_indexer_amd/csrc/attention.hip", "sparse_attention_kv_indexer_amd/csrc/common.h"]
+
+
+def source_digest(sources=SCORE_SOURCES) -> str:
     h = hashlib.sha256()
-    for rel in SCORE_SOURCES:
+    for rel in sources:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def read_traffic(key: str):
-    """HBM bytes per score launch measured with rocprofv3 counters, from the
+def read_traffic(key: str, path: str = TRAFFIC_FILE, sources=SCORE_SOURCES):
+    """HBM bytes per launch measured with rocprofv3 counters, from the
     summary under profiles/, or None when absent or taken on other source."""
-    if not os.path.exists(TRAFFIC_FILE):
+    if not os.path.exists(path):
         return None
     rec = {}
-    for line in open(TRAFFIC_FILE):
+    for line in open(path):
         line = line.strip()
         if line.startswith(key + " "):
             rec = dict(kv.split("=", 1) for kv in line.split()[1:])
-    if rec.get("source_digest") != source_digest():
+    if rec.get("source_digest") != source_digest(sources):
         return None
     return {"read_bytes": int(rec["read_bytes"]), "write_bytes": int(rec["write_bytes"]),
             "total_bytes": int(rec["read_bytes"]) + int(rec["write_bytes"])}
@@ -284,7 +288,8 @@ def bench_attention(args, cfg, inp):
     nsplit = need // (B * wl.ATT_HEADS * (wl.ATT_VD + 1) * 4) if need else 1
     roofline = {
         "bound": "hbm", "kernel": "attention_kernel + merge_kernel (one call)", "achieved": round(achieved, 1),
-        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": read_traffic(cfg.name, ATT_TRAFFIC_FILE, ATT_SOURCES),
         "algorithmic_bytes_per_launch": alg, "launch_avg_us": round(call_ms * 1e3, 3),
     }
     result = {
