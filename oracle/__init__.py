@@ -5,9 +5,9 @@ leg of ``bench.py``; never by the product path. Shares no code with the HIP
 library.
 """
 from .indexer import (PAGE, bf16_bits_to_f64, clamp_len, e4m3_to_f64, gather_keys, score,
-                      score_at, score_fp8, score_magnitudes, score_magnitudes_fp8, sparse_attention,
-                      topk, topk_values)
+                      score_at, score_fp8, score_magnitudes, score_magnitudes_fp8, score_magnitudes_mtp,
+                      score_mtp, sparse_attention, topk, topk_values)
 
 __all__ = ["PAGE", "bf16_bits_to_f64", "clamp_len", "e4m3_to_f64", "gather_keys", "score",
-           "score_at", "score_fp8", "score_magnitudes", "score_magnitudes_fp8",
-           "sparse_attention", "topk", "topk_values"]
+           "score_at", "score_fp8", "score_magnitudes", "score_magnitudes_fp8", "score_magnitudes_mtp",
+           "score_mtp", "sparse_attention", "topk", "topk_values"]

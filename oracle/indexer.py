@@ -211,6 +211,36 @@ def topk_values(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# Several query tokens per request (multi-token prediction / speculative steps)
+# ---------------------------------------------------------------------------
+#
+# Page "The Indexer O(max_context) Breakthrough", section "MTP/EAGLE
+# Integration (Phase 2)": a speculative step scores the current token and its
+# draft tokens together. Reading: each token t of request b is scored exactly
+# as a request of its own, with its own causal length seq_lens[b][t], over the
+# request's pages; the rows are [B][T][width].
+
+def score_mtp(q_bits, w, k_bits, page_table, seq_lens) -> np.ndarray:
+    """Logits [B, T, max_pages * 64] in float64. q_bits uint16 [B, T, H, D];
+    w float32 [B, T, H]; seq_lens int32 [B, T]; k_bits and page_table as for
+    ``score``."""
+    B, T = np.asarray(seq_lens).shape
+    H, D = q_bits.shape[2], q_bits.shape[3]
+    flat = score(q_bits.reshape(B * T, H, D), np.asarray(w).reshape(B * T, H), k_bits,
+                 np.repeat(np.asarray(page_table), T, axis=0), np.asarray(seq_lens).reshape(B * T))
+    return flat.reshape(B, T, -1)
+
+
+def score_magnitudes_mtp(q_bits, w, k_bits, page_table, seq_lens):
+    """``score_magnitudes`` per token row, as [B, T, width] arrays."""
+    B, T = np.asarray(seq_lens).shape
+    H, D = q_bits.shape[2], q_bits.shape[3]
+    M, A = score_magnitudes(q_bits.reshape(B * T, H, D), np.asarray(w).reshape(B * T, H), k_bits,
+                            np.repeat(np.asarray(page_table), T, axis=0), np.asarray(seq_lens).reshape(B * T))
+    return M.reshape(B, T, -1), A.reshape(B, T, -1)
+
+
+# ---------------------------------------------------------------------------
 # Sparse attention over the selected positions (the step after the indexer)
 # ---------------------------------------------------------------------------
 #

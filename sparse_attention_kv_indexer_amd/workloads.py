@@ -288,3 +288,37 @@ def random_selection(inp: Inputs, k: int, seed: int) -> np.ndarray:
         if n:
             out[b, :n] = np.sort(rng.choice(L, size=n, replace=False))
     return out
+
+
+# Several query tokens per request (an input recipe for speculative steps):
+# T bf16 query blocks and T weight vectors per request, drawn like the
+# indexer's (N(0, 1) rounded to bf16; N(0, 1/32)) from PCG64(seed + 2000);
+# token t of a request whose last token sees n = 4 L tokens sees n - (T-1-t)
+# tokens, so its c4 length is (4 L - (T-1-t)) // 4 (the earlier tokens miss
+# the newest c4 position).
+MTP_SEED_OFFSET = 2000
+
+
+@dataclasses.dataclass
+class MtpInputs:
+    """q_bits uint16 [B, T, HEADS, DIM]; w float32 [B, T, HEADS]; seq_lens int32 [B, T]."""
+
+    q_bits: np.ndarray
+    w: np.ndarray
+    seq_lens: np.ndarray
+
+    @property
+    def tokens(self) -> int:
+        return self.q_bits.shape[1]
+
+
+def mtp_inputs(inp: Inputs, tokens: int, seed: int) -> MtpInputs:
+    rng = np.random.Generator(np.random.PCG64(seed + MTP_SEED_OFFSET))
+    B = inp.batch
+    q = _normal_bf16(rng, (B, tokens, HEADS, DIM))
+    w = (rng.standard_normal(B * tokens * HEADS, dtype=np.float32) * np.float32(1.0 / math.sqrt(HEADS)))
+    w = w.reshape(B, tokens, HEADS).astype(np.float32)
+    L = np.asarray(inp.seq_lens, dtype=np.int64)
+    lens = np.stack([np.maximum(4 * L - (tokens - 1 - t), 0) // 4 for t in range(tokens)], axis=1)
+    return MtpInputs(q, w, lens.astype(np.int32))
+
