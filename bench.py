@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--hwm", action="store_true", help="incremental -inf tail (row_hwm) instead of the stateless full tail")
     ap.add_argument("--keys", choices=["bf16", "fp8"], default="bf16",
                     help="key format: bfloat16, or e4m3fn codes with a float32 scale per key")
+    ap.add_argument("--tokens", type=int, default=1,
+                    help="query tokens per request (2..4: a speculative step, every page read once for all of them)")
     ap.add_argument("--stage", choices=["indexer", "attention"], default="indexer",
                     help="indexer: the score + top-k step (default); attention: sparse attention over a "
                          "top-k-shaped selection of the same workload")
@@ -96,22 +98,24 @@ def copy_calibration():
     print(json.dumps({"copy_calibration_bytes": n, "copies": 5}), flush=True)
 
 
-def algorithmic_bytes(inp, hwm: bool) -> dict:
-    """Bytes one score launch must move at minimum: every valid key row, the
-    logits it writes, the page-table entries of valid slots, and q, w and the
-    length of every request."""
+def algorithmic_bytes(inp, hwm: bool, tokens: int = 1, token_lens=None) -> dict:
+    """Bytes one score launch must move at minimum: every valid key row (once,
+    however many query tokens read it), the logits it writes, the page-table
+    entries of valid slots, and q, w and the length of every request and token."""
     import numpy as np
 
     from sparse_attention_kv_indexer_amd import workloads as wl
 
     lens = np.clip(inp.seq_lens.astype(np.int64), 0, inp.max_c4)
+    if token_lens is not None:
+        lens = np.clip(np.asarray(token_lens, dtype=np.int64), 0, inp.max_c4).max(axis=1)
     pages = wl.pages_needed(lens)
     per_key = wl.DIM + 4 if inp.fp8 else wl.DIM * 2  # fp8: 64 codes and a float32 scale
     k_bytes = int(pages.sum()) * wl.PAGE * per_key
-    out_positions = inp.batch * inp.max_c4 if not hwm else int((pages * wl.PAGE).sum())
+    out_positions = tokens * inp.batch * inp.max_c4 if not hwm else int((pages * wl.PAGE).sum())
     out_bytes = out_positions * 4
     table_bytes = int(pages.sum()) * 4
-    req_bytes = inp.batch * (wl.HEADS * wl.DIM * 2 + wl.HEADS * 4 + 4)
+    req_bytes = inp.batch * tokens * (wl.HEADS * wl.DIM * 2 + wl.HEADS * 4 + 4)
     return {"k": k_bytes, "logits": out_bytes, "page_table": table_bytes, "q_w_len": req_bytes,
             "total": k_bytes + out_bytes + table_bytes + req_bytes}
 
@@ -338,26 +342,39 @@ def main():
         torch.cuda.set_device(0)
         bench_attention(args, cfg, inp)
         return
+    T = args.tokens
+    if T != 1 and (args.keys == "fp8" or args.hwm or not 1 <= T <= 4):
+        print("bench.py: --tokens 2..4 runs bf16 keys with the stateless tail", file=sys.stderr)
+        sys.exit(2)
     if args.keys == "fp8":
         inp = wl.to_fp8(inp)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
     base = binding.to_device(inp, dev)
+    mt = None
+    if T > 1:
+        mt = wl.mtp_inputs(inp, T, cfg.seed)
+        base["q"] = torch.from_numpy(mt.q_bits.view("int16")).to(dev).view(torch.bfloat16)
+        base["w"] = torch.from_numpy(mt.w).to(dev)
+        base["seq_lens"] = torch.from_numpy(mt.seq_lens).to(dev)
     B, N, k = inp.batch, inp.max_c4, inp.topk
-    set_bytes = (inp.k8.nbytes + inp.k_scale.nbytes if inp.fp8 else inp.k_bits.nbytes) + B * N * 4
+    set_bytes = (inp.k8.nbytes + inp.k_scale.nbytes if inp.fp8 else inp.k_bits.nbytes) + T * B * N * 4
     R = args.rotate or min(16, max(2, math.ceil(2 * MALL_BYTES / set_bytes)))
     sets = []
     for r in range(R):
         t = {name: (v if r == 0 else v.clone()) for name, v in base.items()}
-        t["logits"] = torch.full((B, N), float("-inf"), dtype=torch.float32, device=dev)
+        t["logits"] = torch.full((B * T, N), float("-inf"), dtype=torch.float32, device=dev)
         t["hwm"] = torch.zeros(B, dtype=torch.int32, device=dev) if args.hwm else None
-        t["idx"] = torch.empty((B, k), dtype=torch.int32, device=dev)
-        t["vals"] = torch.empty((B, k), dtype=torch.float32, device=dev)
+        t["idx"] = torch.empty((B * T, k), dtype=torch.int32, device=dev)
+        t["vals"] = torch.empty((B * T, k), dtype=torch.float32, device=dev)
         sets.append(t)
 
     def launch_score(t):
-        if inp.fp8:
+        if T > 1:
+            binding.score_mtp(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"],
+                              out=t["logits"].view(B, T, N))
+        elif inp.fp8:
             binding.score_fp8(t["q"], t["w"], t["k8"], t["k_scale"], t["page_table"], t["seq_lens"], out=t["logits"],
                               row_hwm=t["hwm"])
         else:
@@ -365,7 +382,7 @@ def main():
                           row_hwm=t["hwm"])
 
     def launch_topk(t):
-        binding.topk(t["logits"], t["seq_lens"], k, out_idx=t["idx"], out_vals=t["vals"])
+        binding.topk(t["logits"], t["seq_lens"].view(-1), k, out_idx=t["idx"], out_vals=t["vals"])
 
     # warm up eagerly once per set (also brings row_hwm to its steady state)
     for t in sets:
@@ -413,11 +430,12 @@ def main():
     score_avg_ms = per_launch_ms(launch_score, n_kern)
     topk_avg_ms = per_launch_ms(launch_topk, n_kern)
 
-    valid = int(np.clip(inp.seq_lens, 0, N).sum())
-    alg = algorithmic_bytes(inp, args.hwm)
+    valid = int(np.clip(inp.seq_lens if mt is None else mt.seq_lens, 0, N).sum())
+    alg = algorithmic_bytes(inp, args.hwm, T, None if mt is None else mt.seq_lens)
     achieved = alg["total"] / (score_avg_ms * 1e-3) / 1e9
     k_only = alg["k"] / (score_avg_ms * 1e-3) / 1e9
-    traffic = read_traffic(args.config + ("+hwm" if args.hwm else "") + ("+fp8" if inp.fp8 else ""))
+    traffic = read_traffic(args.config + ("+hwm" if args.hwm else "") + ("+fp8" if inp.fp8 else "")
+                           + (f"+tok{T}" if T > 1 else ""))
     roofline = {
         "bound": "hbm", "kernel": "score_kernel", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -447,11 +465,15 @@ def main():
             "input_copies": R, "timing": "hipGraph replay of [score; top-k], HIP events",
             "accumulate": "fp32",
             "keys": "e4m3fn codes + float32 scale per key" if inp.fp8 else "bf16",
+            "query_tokens": T,
         },
         "roofline": roofline,
         "cpu_baseline": None,
     }
-    if not args.no_cpu:
+    if T > 1:
+        result["metric"] = METRIC + f" ({T} query tokens per request: token-positions scored/s)"
+        result["unit"] = "valid token-positions/s"
+    if not args.no_cpu and T == 1:
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_reps)
     print(json.dumps(result), flush=True)
 

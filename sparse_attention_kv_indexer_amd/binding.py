@@ -53,6 +53,8 @@ def load() -> ctypes.CDLL:
     lib.dsa_indexer_score.argtypes = [vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, vp]
     lib.dsa_indexer_score_fp8.restype = ctypes.c_int
     lib.dsa_indexer_score_fp8.argtypes = [vp, vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, vp]
+    lib.dsa_indexer_score_mtp.restype = ctypes.c_int
+    lib.dsa_indexer_score_mtp.argtypes = [vp, vp, vp, i64, vp, vp, i32, i32, i32, vp, vp]
     lib.dsa_indexer_topk_workspace_bytes.restype = sz
     lib.dsa_indexer_topk_workspace_bytes.argtypes = [i32, i32, i32]
     lib.dsa_indexer_topk.restype = ctypes.c_int
@@ -155,6 +157,39 @@ def score_fp8(q, w, k8, k_scale, page_table, seq_lens, out=None, row_hwm=None, s
         _stream_ptr(stream))
     if st != 0:
         raise DsaError(st, "dsa_indexer_score_fp8")
+    return out
+
+
+def score_mtp(q, w, k_pool, page_table, seq_lens, out=None, stream=None):
+    """Logits [B, T, max_pages*64] (float32) for T query tokens per request.
+
+    q bf16 [B,T,32,64]; w float32 [B,T,32]; k_pool bf16 [num_pages,64,64];
+    page_table int32 [B,max_pages]; seq_lens int32 [B,T] (each token's
+    length); ``out`` float32 [B,T,max_pages*64] is allocated when not given.
+    """
+    import torch
+
+    B, S = page_table.shape
+    if q.dim() != 4:
+        raise ValueError(f"q has shape {tuple(q.shape)}, expected [B, T, {HEADS}, {DIM}]")
+    T = q.shape[1]
+    dev = q.device
+    bf16 = (torch.bfloat16, torch.int16)
+    _check(q, "q", bf16, (B, T, HEADS, DIM))
+    _check(w, "w", (torch.float32,), (B, T, HEADS), dev)
+    _check(k_pool, "k_pool", bf16, None, dev)
+    if k_pool.dim() != 3 or tuple(k_pool.shape[1:]) != (PAGE, DIM):
+        raise ValueError(f"k_pool has shape {tuple(k_pool.shape)}, expected [num_pages, {PAGE}, {DIM}]")
+    _check(page_table, "page_table", (torch.int32,), None, dev)
+    _check(seq_lens, "seq_lens", (torch.int32,), (B, T), dev)
+    if out is None:
+        out = torch.empty((B, T, S * PAGE), dtype=torch.float32, device=dev)
+    _check(out, "out", (torch.float32,), (B, T, S * PAGE), dev)
+    st = load().dsa_indexer_score_mtp(
+        q.data_ptr(), w.data_ptr(), k_pool.data_ptr(), k_pool.shape[0], page_table.data_ptr(), seq_lens.data_ptr(),
+        B, T, S, out.data_ptr(), _stream_ptr(stream))
+    if st != 0:
+        raise DsaError(st, "dsa_indexer_score_mtp")
     return out
 
 

@@ -33,7 +33,7 @@ const char* dsa_indexer_status_string(int status) {
   switch (status) {
     case DSA_OK: return "ok";
     case DSA_ERR_NULL: return "a required pointer is NULL";
-    case DSA_ERR_SHAPE: return "batch, max_pages, num_pages or max_c4 out of range";
+    case DSA_ERR_SHAPE: return "batch, tokens, max_pages, num_pages, max_c4 or scale out of range";
     case DSA_ERR_ALIGN: return "a pointer misses its required alignment";
     case DSA_ERR_K: return "k out of range (top-k: [1, max_c4]; attention: [1, 2048])";
     case DSA_ERR_WORKSPACE: return "workspace too small";
@@ -54,7 +54,7 @@ int dsa_indexer_score(const void* q, const float* w, const void* k_pool, int64_t
   if (misaligned16(q) || misaligned16(w) || misaligned16(k_pool) || misaligned16(logits) ||
       misaligned4(page_table) || misaligned4(seq_lens) || misaligned4(row_hwm))
     return DSA_ERR_ALIGN;
-  return from_hip(dsa::launch_score(q, w, k_pool, nullptr, num_pages, page_table, seq_lens, batch, max_pages,
+  return from_hip(dsa::launch_score(q, w, k_pool, nullptr, num_pages, page_table, seq_lens, batch, 1, max_pages,
                                     logits, row_hwm, stream));
 }
 
@@ -68,8 +68,22 @@ int dsa_indexer_score_fp8(const void* q, const float* w, const void* k_pool_fp8,
   if (misaligned16(q) || misaligned16(w) || misaligned16(k_pool_fp8) || misaligned16(logits) ||
       misaligned4(k_scale) || misaligned4(page_table) || misaligned4(seq_lens) || misaligned4(row_hwm))
     return DSA_ERR_ALIGN;
-  return from_hip(dsa::launch_score(q, w, k_pool_fp8, k_scale, num_pages, page_table, seq_lens, batch, max_pages,
-                                    logits, row_hwm, stream));
+  return from_hip(dsa::launch_score(q, w, k_pool_fp8, k_scale, num_pages, page_table, seq_lens, batch, 1,
+                                    max_pages, logits, row_hwm, stream));
+}
+
+int dsa_indexer_score_mtp(const void* q, const float* w, const void* k_pool, int64_t num_pages,
+                          const int32_t* page_table, const int32_t* seq_lens, int32_t batch, int32_t tokens,
+                          int32_t max_pages, float* logits, hipStream_t stream) {
+  if (!q || !w || !k_pool || !page_table || !seq_lens || !logits) return DSA_ERR_NULL;
+  if (batch < 1 || batch > kMaxBatch || tokens < 1 || tokens > dsa::kMaxTokens || max_pages < 1 ||
+      max_pages > kMaxPages || num_pages < 1 || (int64_t)batch * tokens * max_pages > kMaxSlots)
+    return DSA_ERR_SHAPE;
+  if (misaligned16(q) || misaligned16(w) || misaligned16(k_pool) || misaligned16(logits) ||
+      misaligned4(page_table) || misaligned4(seq_lens))
+    return DSA_ERR_ALIGN;
+  return from_hip(dsa::launch_score(q, w, k_pool, nullptr, num_pages, page_table, seq_lens, batch, tokens, max_pages,
+                                    logits, nullptr, stream));
 }
 
 size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k) {

@@ -36,10 +36,14 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 constexpr int32_t kMaxRowPositions = 1 << 28;
 
 // Enqueue the score kernel (and, with row_hwm, the high-water-mark update).
-// k_scale == nullptr: bfloat16 keys; otherwise e4m3fn keys with these per-key scales.
+// k_scale == nullptr: bfloat16 keys; otherwise e4m3fn keys with these per-key
+// scales (tokens == 1). tokens (1..4) query tokens per request: q [B][tokens][32][64],
+// w [B][tokens][32], seq_lens [B][tokens], logits [B][tokens][width];
+// row_hwm only with tokens == 1.
+constexpr int32_t kMaxTokens = 4;
 hipError_t launch_score(const void* q, const float* w, const void* k_pool, const float* k_scale,
                         int64_t num_pages, const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
-                        int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream);
+                        int32_t tokens, int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream);
 
 // 32-bit words of top-k workspace for these sizes.
 size_t topk_workspace_words(int32_t batch, int32_t max_c4);

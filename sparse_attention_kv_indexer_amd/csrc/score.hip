@@ -40,13 +40,19 @@
 // conversion is exact: every e4m3 value is a bfloat16 value); the dot
 // products are then multiplied by their key's scale before the ReLU, which is
 // the formula on the scaled key.
+//
+// Several query tokens (score_kernel<false, kTok>, kTok = 2..4: the current
+// token and draft tokens, each with its own causal length): a page is staged
+// once and contracted against each token's query block; the work list covers
+// the pages below the longest of a request's lengths, and each token's row is
+// masked at its own length. Logits are [batch][kTok][width] and the tail is
+// written for every token row (the stateless mode).
 #include "common.h"
 
 namespace dsa {
 namespace {
 
 constexpr int kTailChunk = 4096;  // positions per tail item (16 KiB of -inf)
-constexpr int kWavesPerCU = 12;   // resident one-wave workgroups per CU at this kernel's registers
 
 __device__ __forceinline__ int clamp_len(int len, int width) { return min(max(len, 0), width); }
 
@@ -70,21 +76,24 @@ __device__ __forceinline__ uint32_t wave_total(uint32_t v) {
 }
 
 struct Shape {
-  rsrc_t lens;   // int32 [batch]
-  rsrc_t marks;  // int32 [batch] high-water marks, if `incremental`
+  rsrc_t lens;   // int32 [batch][tok]
+  rsrc_t marks;  // int32 [batch] high-water marks, if `incremental` (tok == 1 only)
   bool incremental;
-  int batch, width;
+  int batch, width, tok;
 };
 
-// Request b's share of the work: its valid pages, and the positions
-// [tail0, tail1) of its -inf tail in chunks of kTailChunk.
+// Request b's share of the work: its valid pages (those below the longest of
+// its tokens' lengths), and the positions [tail0, tail1) of its -inf tail in
+// chunks of kTailChunk.
 struct RowWork {
   uint32_t pages, chunks, tail0, tail1;
 };
 __device__ __forceinline__ RowWork row_work(const Shape& sh, int b) {
   RowWork r{0, 0, 0, 0};
   if (b < sh.batch) {
-    const int len = clamp_len((int)__builtin_amdgcn_raw_buffer_load_b32(sh.lens, b * 4, 0, 0), sh.width);
+    int len = 0;
+    for (int t = 0; t < sh.tok; ++t)
+      len = max(len, clamp_len((int)__builtin_amdgcn_raw_buffer_load_b32(sh.lens, (b * sh.tok + t) * 4, 0, 0), sh.width));
     r.pages = (uint32_t)((len + kPage - 1) / kPage);
     r.tail0 = r.pages * kPage;
     r.tail1 = (uint32_t)sh.width;
@@ -160,25 +169,33 @@ __device__ __forceinline__ bf16x8 e4m3x8_to_bf16(u32x2 x) {
 // distinct banks.
 __device__ __forceinline__ int lds_slot8(int row, int j) { return row * 8 + (j ^ (row & 7)); }
 
-template <bool kFp8>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void score_kernel(
-    const uint16_t* __restrict__ q,          // bf16 [B][32][64]
-    const float* __restrict__ w,             // [B][32]
+// kTok query tokens per request (1: a plain decode step; more: the current
+// token and draft tokens, each with its own causal length), every key page
+// read once for all of them. More tokens hold more query registers, hence
+// fewer resident waves.
+template <int kTok>
+constexpr int waves_per_simd() { return kTok == 1 ? 3 : 2; }
+
+template <bool kFp8, int kTok>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<kTok>(), waves_per_simd<kTok>())))
+void score_kernel(
+    const uint16_t* __restrict__ q,          // bf16 [B][kTok][32][64]
+    const float* __restrict__ w,             // [B][kTok][32]
     const void* __restrict__ k_pool,         // bf16 [num_pages][64][64], or e4m3fn codes [num_pages][64][64]
     const float* __restrict__ k_scale,       // fp8 only: [num_pages][64]
     int64_t num_pages,
     const int32_t* __restrict__ page_table,  // [B][max_pages]
-    const int32_t* __restrict__ seq_lens,    // [B]
+    const int32_t* __restrict__ seq_lens,    // [B][kTok]
     int32_t batch, int32_t max_pages,
-    float* __restrict__ logits,              // [B][max_pages * 64]
-    const int32_t* __restrict__ row_hwm)     // [B] or null
+    float* __restrict__ logits,              // [B][kTok][max_pages * 64]
+    const int32_t* __restrict__ row_hwm)     // [B] or null (kTok == 1 only)
 {
   const int lane = threadIdx.x;
   const int half = lane >> 5;
   const int n = lane & 31;
-  const Shape sh{make_rsrc(seq_lens, (uint32_t)batch * 4u),
-                 make_rsrc(row_hwm != nullptr ? row_hwm : seq_lens, (uint32_t)batch * 4u), row_hwm != nullptr,
-                 batch, max_pages * kPage};
+  const Shape sh{make_rsrc(seq_lens, (uint32_t)(batch * kTok) * 4u),
+                 make_rsrc(row_hwm != nullptr ? row_hwm : seq_lens, (uint32_t)batch * 4u),
+                 kTok == 1 && row_hwm != nullptr, batch, max_pages * kPage, kTok};
 
   // list totals, then this workgroup's contiguous range [s, e)
   uint32_t n_pages = 0, n_chunks = 0;
@@ -239,50 +256,55 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void
     };
 
     int q_row = -1;
-    bf16x8 a[4];
-    f32x4 wv[4];
+    bf16x8 a[kTok][4];
+    f32x4 wv[kTok][4];
     // q and w of request bx, if not held already; called before the phase's
     // other loads, so that waiting for them never waits for those
     auto ensure_qw = [&](int bx) {
       if (bx != q_row) {
         // query operand A (32 heads x 16 dims per step): lane holds head n,
         // dims 16*kb + 8*half .. +7 = chunk 2*kb + half of that head's row
-        const rsrc_t qr = make_rsrc(q + (int64_t)bx * (kHeads * kDim), kHeads * kRowBytes);
+        const rsrc_t qr = make_rsrc(q + (int64_t)bx * (kTok * kHeads * kDim), kTok * kHeads * kRowBytes);
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb)
-          a[kb] = __builtin_bit_cast(bf16x8,
-                                     __builtin_amdgcn_raw_buffer_load_b128(qr, n * kRowBytes + (2 * kb + half) * 16, 0, 0));
+        for (int t = 0; t < kTok; ++t)
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+            a[t][kb] = __builtin_bit_cast(
+                bf16x8, __builtin_amdgcn_raw_buffer_load_b128(
+                            qr, (t * kHeads + n) * kRowBytes + (2 * kb + half) * 16, 0, 0));
         // head weights in accumulator order: register r of a lane holds head
         // 8*(r/4) + 4*half + r%4, so group g = r/4 is the float4 at head 8*g + 4*half
-        const rsrc_t wr = make_rsrc(w + (int64_t)bx * kHeads, kHeads * sizeof(float));
+        const rsrc_t wr = make_rsrc(w + (int64_t)bx * kTok * kHeads, kTok * kHeads * sizeof(float));
 #pragma unroll
-        for (int g = 0; g < 4; ++g)
-          wv[g] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, (8 * g + 4 * half) * 4, 0, 0));
+        for (int t = 0; t < kTok; ++t)
+#pragma unroll
+          for (int g = 0; g < 4; ++g)
+            wv[t][g] = __builtin_bit_cast(
+                f32x4, __builtin_amdgcn_raw_buffer_load_b128(wr, (t * kHeads + 8 * g + 4 * half) * 4, 0, 0));
         q_row = bx;
       }
     };
-    // scores of item (bx, jx) from its key page (q and w of bx held)
+    // scores of item (bx, jx) from its key page (q and w of bx held), for
+    // each of the request's tokens
     auto compute = [&](int bx, uint32_t jx, bool okx, const Regs& page) {
-      const int len = clamp_len(seq_lens[bx], sh.width);
       const int base = (int)jx * kPage;
-      float val = __builtin_nanf("");  // a page id outside the pool scores NaN
+      float val[kTok];
+#pragma unroll
+      for (int t = 0; t < kTok; ++t) val[t] = __builtin_nanf("");  // a page id outside the pool scores NaN
       if (okx) {
-        f32x16 acc0 = {};  // positions 0..31 of the page
-        f32x16 acc1 = {};  // positions 32..63
+        // keys operand B (16 dims x 32 positions per step): lane holds position
+        // n of each half page, dims 16*kb + 8*half .. +7
+        bf16x8 b0[4], b1[4];
         if constexpr (!kFp8) {
           // 16-byte chunk c = 64 * i + lane is key row c / 8, column c % 8
 #pragma unroll
           for (int i = 0; i < Fmt::kLoads; ++i) tile[lds_slot(i * 8 + (lane >> 3), lane & 7)] = page.v[i];
           __syncthreads();
-          // keys operand B (16 dims x 32 positions per step): lane holds position
-          // n of the half page, dims 16*kb + 8*half .. +7
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
             const int col = 2 * kb + half;
-            const bf16x8 b0 = __builtin_bit_cast(bf16x8, tile[lds_slot(n, col)]);
-            const bf16x8 b1 = __builtin_bit_cast(bf16x8, tile[lds_slot(n + 32, col)]);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b1, acc1, 0, 0, 0);
+            b0[kb] = __builtin_bit_cast(bf16x8, tile[lds_slot(n, col)]);
+            b1[kb] = __builtin_bit_cast(bf16x8, tile[lds_slot(n + 32, col)]);
           }
         } else {
           // 16-byte chunk c = 64 * i + lane is key row c / 4, dims 16 * (c % 4) .. +15:
@@ -303,37 +325,51 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void
 #pragma unroll
           for (int kb = 0; kb < 4; ++kb) {
             const int j = 2 * kb + half;
-            const bf16x8 b0 = e4m3x8_to_bf16(tile8[lds_slot8(n, j)]);
-            const bf16x8 b1 = e4m3x8_to_bf16(tile8[lds_slot8(n + 32, j)]);
-            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[kb], b1, acc1, 0, 0, 0);
-          }
-          // each dot product times its key's scale (this lane's keys n and n + 32)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            acc0[r] *= page.s0;
-            acc1[r] *= page.s1;
+            b0[kb] = e4m3x8_to_bf16(tile8[lds_slot8(n, j)]);
+            b1[kb] = e4m3x8_to_bf16(tile8[lds_slot8(n + 32, j)]);
           }
         }
         __syncthreads();  // the tile is rewritten for the next page
-        // weighted ReLU over this lane's 16 heads, then the other 16 from lane ^ 32
-        float p0 = 0.f, p1 = 0.f;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
+        for (int t = 0; t < kTok; ++t) {
+          f32x16 acc0 = {};  // positions 0..31 of the page
+          f32x16 acc1 = {};  // positions 32..63
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            p0 = __builtin_fmaf(wv[g][r], __builtin_fmaxf(acc0[4 * g + r], 0.f), p0);
-            p1 = __builtin_fmaf(wv[g][r], __builtin_fmaxf(acc1[4 * g + r], 0.f), p1);
+          for (int kb = 0; kb < 4; ++kb) {
+            acc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t][kb], b0[kb], acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t][kb], b1[kb], acc1, 0, 0, 0);
           }
+          if constexpr (kFp8) {
+            // each dot product times its key's scale (this lane's keys n and n + 32)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              acc0[r] *= page.s0;
+              acc1[r] *= page.s1;
+            }
+          }
+          // weighted ReLU over this lane's 16 heads, then the other 16 from lane ^ 32
+          float p0 = 0.f, p1 = 0.f;
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              p0 = __builtin_fmaf(wv[t][g][r], __builtin_fmaxf(acc0[4 * g + r], 0.f), p0);
+              p1 = __builtin_fmaf(wv[t][g][r], __builtin_fmaxf(acc1[4 * g + r], 0.f), p1);
+            }
+          }
+          p0 += __shfl_xor(p0, 32);
+          p1 += __shfl_xor(p1, 32);
+          // lane < 32 owns position lane of the first half, lane >= 32 position lane of the second
+          val[t] = half ? p1 : p0;
         }
-        p0 += __shfl_xor(p0, 32);
-        p1 += __shfl_xor(p1, 32);
-        // lane < 32 owns position lane of the first half, lane >= 32 position lane of the second
-        val = half ? p1 : p0;
       }
-      if (base + lane >= len) val = -__builtin_inff();  // partial last page
-      const rsrc_t out = make_rsrc(logits + (int64_t)bx * sh.width + base, kPage * sizeof(float));
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val), out, lane * 4, 0, 0);
+#pragma unroll
+      for (int t = 0; t < kTok; ++t) {
+        const int len = clamp_len(seq_lens[bx * kTok + t], sh.width);
+        const float v = base + lane >= len ? -__builtin_inff() : val[t];  // partial last page, shorter tokens
+        const rsrc_t out = make_rsrc(logits + ((int64_t)bx * kTok + t) * sh.width + base, kPage * sizeof(float));
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), out, lane * 4, 0, 0);
+      }
     };
 
     // state at the top of each half of the loop, for the item `it` it computes:
@@ -377,12 +413,15 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(3, 3))) void
       window_find(W, it - n_pages, sh, true, b, c);
       const RowWork r = row_work(sh, b);
       const uint32_t c0 = r.tail0 + c * kTailChunk, c1 = min(r.tail1, c0 + kTailChunk);
-      const rsrc_t row = make_rsrc(logits + (int64_t)b * sh.width, (uint32_t)sh.width * 4u);
-      // c0 and c1 are multiples of 4 (page and row boundaries): whole 16-byte stores
-      // streaming stores: the tail is not read back soon (measured: faster where the tail dominates,
-      // unchanged elsewhere; the scored pages keep ordinary stores, which the top-k reads next)
-      for (uint32_t p = c0 + 4 * lane; p < c1; p += 256)
-        __builtin_amdgcn_raw_buffer_store_b128(ninf, row, p * 4, 0, kNonTemporal);
+#pragma unroll
+      for (int t = 0; t < kTok; ++t) {
+        const rsrc_t row = make_rsrc(logits + ((int64_t)b * kTok + t) * sh.width, (uint32_t)sh.width * 4u);
+        // c0 and c1 are multiples of 4 (page and row boundaries): whole 16-byte stores
+        // streaming stores: the tail is not read back soon (measured: faster where the tail dominates,
+        // unchanged elsewhere; the scored pages keep ordinary stores, which the top-k reads next)
+        for (uint32_t p = c0 + 4 * lane; p < c1; p += 256)
+          __builtin_amdgcn_raw_buffer_store_b128(ninf, row, p * 4, 0, kNonTemporal);
+      }
     }
   }
 }
@@ -417,21 +456,51 @@ int cu_count(hipStream_t stream) {
 
 }  // namespace
 
+namespace {
+
+template <bool kFp8, int kTok>
+void launch_variant(int grid, hipStream_t stream, const void* q, const float* w, const void* k_pool,
+                    const float* k_scale, int64_t num_pages, const int32_t* page_table, const int32_t* seq_lens,
+                    int32_t batch, int32_t max_pages, float* logits, int32_t* row_hwm) {
+  hipLaunchKernelGGL((score_kernel<kFp8, kTok>), dim3(grid), dim3(64), 0, stream, static_cast<const uint16_t*>(q),
+                     w, k_pool, k_scale, num_pages, page_table, seq_lens, batch, max_pages, logits, row_hwm);
+}
+
+}  // namespace
+
 hipError_t launch_score(const void* q, const float* w, const void* k_pool, const float* k_scale,
                         int64_t num_pages, const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
-                        int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream) {
+                        int32_t tokens, int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream) {
   // as many one-wave workgroups as stay resident, but no more than the largest
   // list these shapes allow (every slot a page, plus every tail chunk)
   const int64_t width = (int64_t)max_pages * kPage;
   const int64_t most = (int64_t)batch * max_pages + (int64_t)batch * ((width + kTailChunk - 1) / kTailChunk);
-  const int grid = (int)std::min<int64_t>((int64_t)cu_count(stream) * kWavesPerCU, most);
-  if (k_scale != nullptr)
-    hipLaunchKernelGGL(score_kernel<true>, dim3(grid), dim3(64), 0, stream, static_cast<const uint16_t*>(q), w, k_pool,
-                       k_scale, num_pages, page_table, seq_lens, batch, max_pages, logits, row_hwm);
-  else
-    hipLaunchKernelGGL(score_kernel<false>, dim3(grid), dim3(64), 0, stream, static_cast<const uint16_t*>(q), w, k_pool,
-                       k_scale, num_pages, page_table, seq_lens, batch, max_pages, logits, row_hwm);
-  if (row_hwm != nullptr) {
+  const int per_cu = 4 * (tokens == 1 ? waves_per_simd<1>() : waves_per_simd<2>());
+  const int grid = (int)std::min<int64_t>((int64_t)cu_count(stream) * per_cu, most);
+  if (k_scale != nullptr) {
+    launch_variant<true, 1>(grid, stream, q, w, k_pool, k_scale, num_pages, page_table, seq_lens, batch, max_pages,
+                            logits, row_hwm);
+  } else {
+    switch (tokens) {
+      case 1:
+        launch_variant<false, 1>(grid, stream, q, w, k_pool, k_scale, num_pages, page_table, seq_lens, batch,
+                                 max_pages, logits, row_hwm);
+        break;
+      case 2:
+        launch_variant<false, 2>(grid, stream, q, w, k_pool, k_scale, num_pages, page_table, seq_lens, batch,
+                                 max_pages, logits, nullptr);
+        break;
+      case 3:
+        launch_variant<false, 3>(grid, stream, q, w, k_pool, k_scale, num_pages, page_table, seq_lens, batch,
+                                 max_pages, logits, nullptr);
+        break;
+      default:
+        launch_variant<false, 4>(grid, stream, q, w, k_pool, k_scale, num_pages, page_table, seq_lens, batch,
+                                 max_pages, logits, nullptr);
+        break;
+    }
+  }
+  if (row_hwm != nullptr && tokens == 1) {
     // after every workgroup of the score kernel has read the old marks
     hipLaunchKernelGGL(hwm_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, seq_lens, batch,
                        max_pages * kPage, row_hwm);

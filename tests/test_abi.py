@@ -29,13 +29,13 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for name in names:
         assert hasattr(lib, name), f"{name} not exported"
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dsa_indexer_abi_version() == 3
+    assert lib.dsa_indexer_abi_version() == 4
     for st in (OK, NULL, SHAPE, ALIGN, K, WS, -6):
         assert lib.dsa_indexer_status_string(st).decode() not in ("", "unknown status")
     assert lib.dsa_indexer_status_string(12345).decode() == "unknown status"
@@ -157,3 +157,27 @@ def test_attention_workspace_contract(lib):
     assert lib.dsa_indexer_sparse_attention_workspace_bytes(4, 4096) == 0  # k out of range
     assert lib.dsa_indexer_sparse_attention(*att_args(batch=64, k=2048, ws_bytes=need - 1)) == WS
     assert lib.dsa_indexer_sparse_attention(*att_args(batch=64, k=2048, workspace=None, ws_bytes=need)) == WS
+
+
+def mtp_args(**over):
+    args = dict(q=A, w=A, k_pool=A, num_pages=4, page_table=A, seq_lens=A, batch=2, tokens=2, max_pages=3, logits=A,
+                stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("field", ["q", "w", "k_pool", "page_table", "seq_lens", "logits"])
+def test_score_mtp_null(lib, field):
+    assert lib.dsa_indexer_score_mtp(*mtp_args(**{field: None})) == NULL
+
+
+@pytest.mark.parametrize("over", [dict(batch=0), dict(batch=65536), dict(tokens=0), dict(tokens=5), dict(max_pages=0),
+                                  dict(max_pages=(1 << 22) + 1), dict(num_pages=0),
+                                  dict(batch=64, tokens=4, max_pages=(1 << 18) + 1)])
+def test_score_mtp_shape(lib, over):
+    assert lib.dsa_indexer_score_mtp(*mtp_args(**over)) == SHAPE
+
+
+@pytest.mark.parametrize("field,off", [("q", 8), ("w", 4), ("k_pool", 2), ("logits", 4), ("page_table", 2), ("seq_lens", 1)])
+def test_score_mtp_alignment(lib, field, off):
+    assert lib.dsa_indexer_score_mtp(*mtp_args(**{field: A + off})) == ALIGN
