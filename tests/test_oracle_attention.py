@@ -125,3 +125,19 @@ def test_selection_recipe():
         row = sel[b]
         assert np.all(row[n:] == -1)
         assert np.all(np.diff(row[:n]) > 0) and (n == 0 or (row[0] >= 0 and row[n - 1] < L))
+
+
+def test_a_repeated_position_counts_twice():
+    """Selection [s, s, t]: weights e^a, e^a, e^b (closed form with two distinct latents)."""
+    inp, q, kv, idx = _case(8, B=1, k=3)
+    s_, t_ = int(idx[0, 0]), int(idx[0, 1])
+    sel = np.array([[s_, s_, t_]], dtype=np.int64)
+    out, lse = oracle.sparse_attention(q, kv, inp.page_table, sel, 0.3, 8)
+    qf = oracle.bf16_bits_to_f64(q)[0]
+    kf = oracle.bf16_bits_to_f64(kv)
+    vs = kf[inp.page_table[0, s_ // 64], s_ % 64]
+    vt = kf[inp.page_table[0, t_ // 64], t_ % 64]
+    a, b = 0.3 * (qf @ vs), 0.3 * (qf @ vt)  # [H]
+    want = (2 * np.exp(a)[:, None] * vs[None, :8] + np.exp(b)[:, None] * vt[None, :8]) / (2 * np.exp(a) + np.exp(b))[:, None]
+    assert np.allclose(out[0], want, rtol=0, atol=1e-12)
+    assert np.allclose(lse[0], np.log(2 * np.exp(a) + np.exp(b)), rtol=0, atol=1e-12)
