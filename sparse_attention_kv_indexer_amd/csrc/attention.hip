@@ -8,26 +8,28 @@
 // 64 positions, found through the same page table as the indexer keys.
 //
 // attention_kernel: one 256-thread workgroup per (request, split), where a
-// split is a run of at most `chunk` entries of the request's list. It
-// processes tiles of 32 positions, double-buffered in LDS:
-//   - staging: each thread copies 144 B of one latent row with 16-byte loads
-//     (a wave's load covers 8 rows of 128 B lines), issued one tile ahead and
-//     written to the LDS buffer the previous tile has released. Rows are
-//     stored as 72 chunks of 16 B, with chunk c of row r at c ^ swz(r), which
-//     keeps every LDS access pattern below free of bank conflicts;
-//   - wave (hh, dh) owns heads 16hh..16hh+15 and value dims 256dh..256dh+255.
-//     It computes S^T for all 32 tile positions of its heads over the 576
-//     dims with v_mfma_f32_16x16x32_bf16 (its queries held in registers; the
-//     two waves of a head half compute the same scores), so its softmax needs
-//     nothing from other waves;
-//   - online softmax in base 2, per wave: the output is rescaled only when a
-//     head's maximum grows by more than 8 (exact either way, as the output
-//     and the sum of weights share the reference). The weights, rounded to
-//     bf16, sit in the registers in the B-operand layout of the value product;
-//   - O^T += V^T P^T, again on 16x16x32 blocks: V^T comes straight from the
-//     staged rows through ds_read_b64_tr_b16 (each 16-lane group reads a
-//     4 x 16 block of bf16 and receives it transposed).
-// One barrier per tile: the staged buffer of the next tile is complete.
+// split is a run of at most `chunk` entries of the request's list, on one CU.
+// It processes tiles of 32 positions:
+//   - staging: direct-to-LDS loads (global_load_lds_dwordx4) into four tile
+//     buffers, up to four tiles ahead. Rows are stored as 72 chunks of 16 B,
+//     with chunk c of row r at c ^ swz(r);
+//   - scores: wave (ph, hh) computes the 16 positions x 16 heads block
+//     (positions 16ph.., heads 16hh..) of S^T over the 576 dims with
+//     v_mfma_f32_16x16x32_bf16 (its 16 heads' queries held in registers) and
+//     publishes it with its per-head maxima to a score tile in LDS;
+//   - softmax: every wave reads the whole 32 x 32 score tile and runs the same
+//     online softmax in base 2, so no other agreement between waves is
+//     needed; the output is rescaled only when a head's maximum grows by more
+//     than 8 (exact either way, as the output and the sum of weights share
+//     the reference). The weights, rounded to bf16, sit in the registers in
+//     the B-operand layout of the value product;
+//   - values: wave wv owns value dims 128wv..128wv+127 for all 32 heads:
+//     O^T (16 dims x 16 heads blocks) += V^T P^T on 16x16x32 MFMAs, V^T read
+//     straight from the staged rows with ds_read_b64_tr_b16 (each 16-lane
+//     group reads a 4 x 16 block of bf16 and receives it transposed); each
+//     transposed read feeds both head blocks.
+// The steps are software-pipelined (the softmax of tile t, the scores of tile
+// t+1 and the values of tile t in one step), with one barrier per tile.
 // With one split the kernel writes the normalised output and the log-sum-exp
 // directly. Otherwise it writes each split's normalised partial output and
 // log-sum-exp to the workspace, and merge_kernel combines them.
@@ -48,6 +50,7 @@ constexpr int kTile = 32;                      // positions per tile
 constexpr int kTileBytes = kTile * kLatBytes;  // 36 KiB
 constexpr int kBufs = 4;                       // staged tiles: one computed, three loading
 constexpr int kSRow = 36;                      // floats per row (head) of the score tile: 32 + padding
+constexpr int kSTile = kAttHeads * kSRow;
 constexpr int kAttThreads = 256;
 constexpr int kAttWaves = kAttThreads / 64;
 constexpr int kQSteps = kKD / 32;              // 18 k-steps of the 16x16x32 MFMA
@@ -97,13 +100,12 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
 
 __device__ __forceinline__ float xor_lanes(float v, int m) { return __shfl_xor(v, m, 64); }
 
-// Chunk c of staged row r sits at chunk c ^ swz(r) of that row. Over any 16
-// aligned rows, swz takes each value once on the even and once on the odd
-// rows and once on each aligned 8; swz >> 1 differs on any aligned 4 rows.
-// So reads of one chunk from 16 rows (scores) and of 32 B from 4 or 8 rows
-// (the transposed value reads) never share a bank, whether the LDS serves
-// 128 or 256 bytes per clock.
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) ^ (3 * ((r >> 2) & 1)) ^ ((r >> 3) & 1); }
+// Chunk c of staged row r sits at chunk c ^ (r & 7) of that row: the rows of
+// an aligned group of 8 put any given chunk in 8 different 16-byte slots of
+// one 128-byte span. Measured on gfx950 with the kernel's access patterns:
+// the 16-row score reads then run at the speed of contiguous 16-byte reads,
+// and the transposed value reads at their own full rate.
+__device__ __forceinline__ int swz(int r) { return r & 7; }
 
 // 4 bf16 of LDS, transposed across each 16-lane group.
 __device__ __forceinline__ u32x2 read_tr(const unsigned char* p) {
@@ -156,8 +158,8 @@ __global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(1, 
 void attention_kernel(const AttArgs a) {
   // Tile t is staged in buffer t % 4 while tiles t+1 .. t+3 are loading.
   __shared__ __attribute__((aligned(16))) unsigned char tbuf[kBufs * kTileBytes];
-  __shared__ __attribute__((aligned(16))) float sbuf[kAttHeads * kSRow];
-  __shared__ float mbuf[2][kAttHeads];
+  __shared__ __attribute__((aligned(16))) float sbuf[2 * kSTile];  // score tiles of two consecutive tiles
+  __shared__ float mbuf[2][2][kAttHeads];                           // [tile % 2][position half][head] maxima
   __shared__ uint32_t rows[kMaxAttChunk];
 
   int b, s;
@@ -257,17 +259,21 @@ void attention_kernel(const AttArgs a) {
     for (int db = 0; db < 8; ++db) O[hb][db] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run[2] = {-__builtin_inff(), -__builtin_inff()}, l_run[2] = {0.f, 0.f};
 
-  auto compute = [&](const unsigned char* cur, int t) {
+  // Scores of tile t (this wave's 16 x 16 block) into score buffer t % 2.
+  auto scores = [&](const unsigned char* cur, int t) {
     f32x4 S0 = {0.f, 0.f, 0.f, 0.f}, S1 = S0;
-    {
-      u32x4 kx[kQSteps];
 #pragma unroll
-      for (int st = 0; st < kQSteps; ++st)
-        kx[st] = *reinterpret_cast<const u32x4*>(cur + ((st & 1) ? kofs_odd : kofs_even) + 64 * (st & ~1));
+    for (int s0 = 0; s0 < kQSteps; s0 += 6) {  // six operand reads in flight, then six MFMAs
+      u32x4 kx[6];
 #pragma unroll
-      for (int st = 0; st < kQSteps; st += 2) {
-        S0 = mfma16(kx[st], qv[st], S0);
-        S1 = mfma16(kx[st + 1], qv[st + 1], S1);
+      for (int i = 0; i < 6; ++i) {
+        const int st = s0 + i;
+        kx[i] = *reinterpret_cast<const u32x4*>(cur + ((st & 1) ? kofs_odd : kofs_even) + 64 * (st & ~1));
+      }
+#pragma unroll
+      for (int i = 0; i < 6; i += 2) {
+        S0 = mfma16(kx[i], qv[s0 + i], S0);
+        S1 = mfma16(kx[i + 1], qv[s0 + i + 1], S1);
       }
     }
     // Register r: tile position 16ph + 4g + r, head 16hh + j.
@@ -282,19 +288,21 @@ void attention_kernel(const AttArgs a) {
     }
     mt = fmaxf(mt, xor_lanes(mt, 16));
     mt = fmaxf(mt, xor_lanes(mt, 32));
-    *reinterpret_cast<f32x4*>(sbuf + s_wr) = S;
-    if (g == 0) mbuf[ph][16 * hh + j] = mt;
-    lds_barrier();
+    *reinterpret_cast<f32x4*>(sbuf + (t & 1) * kSTile + s_wr) = S;
+    if (g == 0) mbuf[t & 1][ph][16 * hh + j] = mt;
+  };
 
-    // Softmax over the tile for heads j (hb = 0) and 16 + j (hb = 1): this
-    // lane's positions 8g..8g+7.
-    u32x4 P[2];
+  // Softmax of tile t (score buffer t % 2, complete in every wave) for heads
+  // j (hb = 0) and 16 + j (hb = 1) at this lane's positions 8g..8g+7: the
+  // B operands of the value product, rescaling O when a maximum grows.
+  auto softmax = [&](int t, u32x4 (&P)[2]) {
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       const int h = 16 * hb + j;
-      const f32x4 x0 = *reinterpret_cast<const f32x4*>(sbuf + h * kSRow + 8 * g);
-      const f32x4 x1 = *reinterpret_cast<const f32x4*>(sbuf + h * kSRow + 8 * g + 4);
-      const float tm = fmaxf(mbuf[0][h], mbuf[1][h]);
+      const float* sb = sbuf + (t & 1) * kSTile + h * kSRow + 8 * g;
+      const f32x4 x0 = *reinterpret_cast<const f32x4*>(sb);
+      const f32x4 x1 = *reinterpret_cast<const f32x4*>(sb + 4);
+      const float tm = fmaxf(mbuf[t & 1][0][h], mbuf[t & 1][1][h]);
       if (__any(tm > m_run[hb] + kRegrow)) {
         const float mn = fmaxf(m_run[hb], tm);
         const float alpha = m_run[hb] == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f(m_run[hb] - mn);
@@ -309,38 +317,70 @@ void attention_kernel(const AttArgs a) {
       P[hb][2] = pack_bf16(__builtin_amdgcn_exp2f(x1[0] - ref), __builtin_amdgcn_exp2f(x1[1] - ref), l_run[hb]);
       P[hb][3] = pack_bf16(__builtin_amdgcn_exp2f(x1[2] - ref), __builtin_amdgcn_exp2f(x1[3] - ref), l_run[hb]);
     }
+  };
 
-    // O^T += V^T P^T: each V^T block feeds both head blocks.
-    u32x4 va[8];
+  // O^T += V^T P^T over tile `cur`: each V^T block feeds both head blocks.
+  auto values = [&](const unsigned char* cur, const u32x4 (&P)[2]) {
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      const u32x2 lo = read_tr(cur + vb[0] + 128 * (db >> 2) + vx[0][db & 3]);
-      const u32x2 hi = read_tr(cur + vb[1] + 128 * (db >> 2) + vx[1][db & 3]);
-      va[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
-    }
+    for (int d0 = 0; d0 < 8; d0 += 4) {
+      u32x4 va[4];
 #pragma unroll
-    for (int db = 0; db < 8; ++db) {
-      O[0][db] = mfma16(va[db], P[0], O[0][db]);
-      O[1][db] = mfma16(va[db], P[1], O[1][db]);
+      for (int i = 0; i < 4; ++i) {
+        const int db = d0 + i;
+        const u32x2 lo = read_tr(cur + vb[0] + 128 * (db >> 2) + vx[0][db & 3]);
+        const u32x2 hi = read_tr(cur + vb[1] + 128 * (db >> 2) + vx[1][db & 3]);
+        va[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        O[0][d0 + i] = mfma16(va[i], P[0], O[0][d0 + i]);
+        O[1][d0 + i] = mfma16(va[i], P[1], O[1][d0 + i]);
+      }
     }
   };
 
-  // Tile t: wait for this wave's loads of it (those of tiles t+1, t+2 may
-  // still be in flight) and for its LDS accesses, barrier (everyone's loads
-  // of tile t have landed, and everyone is done with tile t-1), refill tile
-  // t-1's buffer with tile t+3, compute tile t.
+  // Software pipeline over the tiles, one barrier per step. Step t: the
+  // softmax of tile t (its scores were published in step t-1), the scores of
+  // tile t+1 and the values of tile t, three independent streams the
+  // compiler interleaves; then wait for this wave's loads of tile t+2 and its
+  // LDS accesses, barrier (tile t+1's scores are complete, tile t+2 has
+  // landed, every wave is done with tile t), and refill tile t's buffer with
+  // tile t+4. The prologue loads tiles 0..3 and publishes tile 0's scores.
+  auto tbuf_of = [&](int t) { return tbuf + (t & (kBufs - 1)) * kTileBytes; };
   __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));  // the queries have landed; only tile loads are outstanding below
-  for (int t = 0; t < kBufs - 1 && t < ntiles; ++t) stage(t, t);
-  for (int t = 0; t < ntiles; ++t) {
-    if (t + 2 < ntiles)
+  for (int t = 0; t < kBufs && t < ntiles; ++t) stage(t, t);
+  {
+    const int later = min(kBufs, ntiles) - 1;  // tiles 1.. already loading
+    if (later >= 3)
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(3 * kStage));
+    else if (later == 2)
       __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * kStage));
-    else if (t + 1 < ntiles)
+    else if (later == 1)
       __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(kStage));
     else
       __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
     __builtin_amdgcn_s_barrier();
-    if (t + 3 < ntiles) stage((t + 3) & (kBufs - 1), t + 3);
-    compute(tbuf + (t & (kBufs - 1)) * kTileBytes, t);
+    scores(tbuf_of(0), 0);
+    if (later >= 3)
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * kStage));
+    else if (later == 2)
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(kStage));
+    else
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+    __builtin_amdgcn_s_barrier();
+  }
+  for (int t = 0; t < ntiles; ++t) {
+    u32x4 P[2];
+    softmax(t, P);
+    if (t + 1 < ntiles) scores(tbuf_of(t + 1), t + 1);
+    values(tbuf_of(t), P);
+    // tile t+2 must have landed; tile t+3's loads may still be in flight
+    if (t + 3 < ntiles)
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(kStage));
+    else
+      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+    __builtin_amdgcn_s_barrier();
+    if (t + kBufs < ntiles) stage(t & (kBufs - 1), t + kBufs);
   }
 
   // Sums of weights of this lane's two heads over all lanes (g) of the wave.
