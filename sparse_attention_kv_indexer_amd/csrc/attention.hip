@@ -57,6 +57,7 @@ constexpr int kQSteps = kKD / 32;              // 18 k-steps of the 16x16x32 MFM
 constexpr int kStage = kLatBytes / 128;        // 9 loads of 16 B per thread per tile
 constexpr int kMergeThreads = 256;
 constexpr int kMergeParts = kAttHeads * kVD / 4 / kMergeThreads;  // 16 workgroups per request
+constexpr int kMergeBatch = 8;                 // splits whose partials one merge thread loads at once
 constexpr uint32_t kSkip = 0xFFFFFFFFu;        // row code: list entry not attended
 constexpr uint32_t kBad = 0xFFFFFFFEu;         // row code: entry past the table or on a page outside the pool
 constexpr float kRegrow = 8.0f;                // log2 headroom of the weights over the running maximum
@@ -434,24 +435,45 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const AttArgs a) {
   const int ns = a.nsplit;
   const rsrc_t lr = make_rsrc(a.part_lse + (int64_t)b * ns * kAttHeads, (uint32_t)ns * kAttHeads * 4u);
   const rsrc_t orr = make_rsrc(a.part_o + (int64_t)b * ns * kAttHeads * kVD, (uint32_t)ns * kAttHeads * kVD * 4u);
+  // The partial outputs are loaded with the log-sum-exps (eight splits at a
+  // time), not after their maximum is known: one memory round trip, not two.
   float M = -__builtin_inff();
   bool nan = false;
-  for (int s = 0; s < ns; ++s) {
-    const float x = __builtin_bit_cast(float, load_u32(lr, (s * kAttHeads + h) * 4));
-    nan |= x != x;
-    M = fmaxf(M, x);
-  }
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float wsum = 0.f;
-  if (M > -__builtin_inff()) {
-    for (int s = 0; s < ns; ++s) {
-      const float x = __builtin_bit_cast(float, load_u32(lr, (s * kAttHeads + h) * 4));
-      const float wt = __builtin_amdgcn_exp2f((x - M) * 1.44269504088896341f);
-      const f32x4 o = __builtin_bit_cast(
-          f32x4, __builtin_amdgcn_raw_buffer_load_b128(orr, ((s * kAttHeads + h) * kVD + d) * 4, 0, 0));
-      acc += o * wt;
-      wsum += wt;
+  for (int s0 = 0; s0 < ns; s0 += kMergeBatch) {
+    float x[kMergeBatch];
+    f32x4 o[kMergeBatch];
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int sx = min(s0 + i, ns - 1);  // repeats of the last split are not accumulated
+      x[i] = __builtin_bit_cast(float, load_u32(lr, (sx * kAttHeads + h) * 4));
+      o[i] = __builtin_bit_cast(f32x4,
+                                __builtin_amdgcn_raw_buffer_load_b128(orr, ((sx * kAttHeads + h) * kVD + d) * 4, 0, 0));
     }
+    float Mb = M;
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      if (s0 + i < ns) {
+        nan |= x[i] != x[i];
+        Mb = fmaxf(Mb, x[i]);
+      }
+    }
+    if (Mb > -__builtin_inff()) {
+      // rebase what was accumulated so far to the new maximum, then add this batch
+      const float r = M == -__builtin_inff() ? 0.f : __builtin_amdgcn_exp2f((M - Mb) * 1.44269504088896341f);
+      acc *= r;
+      wsum *= r;
+#pragma unroll
+      for (int i = 0; i < kMergeBatch; ++i) {
+        if (s0 + i < ns) {
+          const float wt = __builtin_amdgcn_exp2f((x[i] - Mb) * 1.44269504088896341f);
+          acc += o[i] * wt;
+          wsum += wt;
+        }
+      }
+    }
+    M = Mb;
   }
   float inv = wsum > 0.f ? 1.0f / wsum : 0.f;
   float l = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -__builtin_inff();
