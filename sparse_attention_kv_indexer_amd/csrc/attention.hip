@@ -52,7 +52,6 @@ constexpr int kBufs = 4;                       // staged tiles: one computed, th
 constexpr int kSRow = 36;                      // floats per row (head) of the score tile: 32 + padding
 constexpr int kSTile = kAttHeads * kSRow;
 constexpr int kAttThreads = 256;
-constexpr int kAttWaves = kAttThreads / 64;
 constexpr int kQSteps = kKD / 32;              // 18 k-steps of the 16x16x32 MFMA
 constexpr int kStage = kLatBytes / 128;        // 9 loads of 16 B per thread per tile
 constexpr int kMergeThreads = 256;
@@ -87,11 +86,6 @@ struct AttArgs {
 
 __device__ __forceinline__ uint32_t load_u32(rsrc_t r, int off) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
-}
-
-__device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b),
-                                                 c, 0, 0, 0);
 }
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
@@ -146,14 +140,6 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
 // Encoding of s_waitcnt that waits until at most n vector-memory operations
 // and no LDS operations of this wave are outstanding.
 constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8); }
-constexpr int kLgkmWait = vm_lgkm_wait(63);  // LDS only
-
-// Workgroup barrier after this wave's LDS accesses have completed (a bare
-// s_barrier does not wait for them).
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(kLgkmWait);
-  __builtin_amdgcn_s_barrier();
-}
 
 __global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void attention_kernel(const AttArgs a) {

@@ -118,11 +118,6 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
   return v;
 }
 
-// Lanes of this wave below the calling one whose bit is set in mask.
-__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
-  return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-}
-
 // Inclusive scans of a and b over the workgroup's lanes in lane order, and
 // their totals; `part` is 2 * kWaves words of LDS. Every lane must call it;
 // it ends with a barrier, after which part may be rewritten.
