@@ -48,6 +48,9 @@ def parse():
     ap.add_argument("--stage", choices=["indexer", "attention"], default="indexer",
                     help="indexer: the score + top-k step (default); attention: sparse attention over a "
                          "top-k-shaped selection of the same workload")
+    ap.add_argument("--topk", choices=["hist", "sampled"], default="sampled",
+                    help="hist: the score kernel counts each row's first-digit histogram and the top-k starts "
+                         "from it (score_hist + topk_hist); sampled: the top-k samples its own cut")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-reps", type=int, default=3)
     ap.add_argument("--copy-calibration", action="store_true",
@@ -346,6 +349,10 @@ def main():
     if T != 1 and (args.keys == "fp8" or args.hwm or not 1 <= T <= 4):
         print("bench.py: --tokens 2..4 runs bf16 keys with the stateless tail", file=sys.stderr)
         sys.exit(2)
+    fused = args.topk == "hist"
+    if fused and (T != 1 or args.keys == "fp8"):
+        print("bench.py: --topk hist runs one query token with bf16 keys", file=sys.stderr)
+        sys.exit(2)
     if args.keys == "fp8":
         inp = wl.to_fp8(inp)
     dev = torch.device("cuda:0")
@@ -368,6 +375,7 @@ def main():
         t["hwm"] = torch.zeros(B, dtype=torch.int32, device=dev) if args.hwm else None
         t["idx"] = torch.empty((B * T, k), dtype=torch.int32, device=dev)
         t["vals"] = torch.empty((B * T, k), dtype=torch.float32, device=dev)
+        t["hist"] = binding.hist_buffer(B, dev) if fused else None
         sets.append(t)
 
     def launch_score(t):
@@ -377,12 +385,19 @@ def main():
         elif inp.fp8:
             binding.score_fp8(t["q"], t["w"], t["k8"], t["k_scale"], t["page_table"], t["seq_lens"], out=t["logits"],
                               row_hwm=t["hwm"])
+        elif fused:
+            binding.score_hist(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"], t["hist"],
+                               out=t["logits"], row_hwm=t["hwm"])
         else:
             binding.score(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"], out=t["logits"],
                           row_hwm=t["hwm"])
 
     def launch_topk(t):
-        binding.topk(t["logits"], t["seq_lens"].view(-1), k, out_idx=t["idx"], out_vals=t["vals"])
+        binding.topk(t["logits"], t["seq_lens"].view(-1), k, out_idx=t["idx"], out_vals=t["vals"], hist=t["hist"])
+
+    def launch_step(t):
+        launch_score(t)
+        launch_topk(t)
 
     # warm up eagerly once per set (also brings row_hwm to its steady state)
     for t in sets:
@@ -427,21 +442,31 @@ def main():
         return s.elapsed_time(e) / n
 
     n_kern = max(10, min(args.steps, 200))
-    score_avg_ms = per_launch_ms(launch_score, n_kern)
-    topk_avg_ms = per_launch_ms(launch_topk, n_kern)
+    if fused:
+        # the top-k consumes (and zeroes) the histogram its score call filled, so
+        # it is timed as whole steps minus the score kernel alone; the score
+        # kernel's own back-to-back launches leave the histograms dirty, so
+        # they go last
+        step_avg_ms = per_launch_ms(launch_step, n_kern)
+        score_avg_ms = per_launch_ms(launch_score, n_kern)
+        topk_avg_ms = step_avg_ms - score_avg_ms
+    else:
+        score_avg_ms = per_launch_ms(launch_score, n_kern)
+        topk_avg_ms = per_launch_ms(launch_topk, n_kern)
 
     valid = int(np.clip(inp.seq_lens if mt is None else mt.seq_lens, 0, N).sum())
     alg = algorithmic_bytes(inp, args.hwm, T, None if mt is None else mt.seq_lens)
     achieved = alg["total"] / (score_avg_ms * 1e-3) / 1e9
     k_only = alg["k"] / (score_avg_ms * 1e-3) / 1e9
     traffic = read_traffic(args.config + ("+hwm" if args.hwm else "") + ("+fp8" if inp.fp8 else "")
-                           + (f"+tok{T}" if T > 1 else ""))
+                           + (f"+tok{T}" if T > 1 else "") + ("+hist" if fused else ""))
     roofline = {
         "bound": "hbm", "kernel": "score_kernel", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
         "algorithmic_bytes_per_launch": alg, "launch_avg_us": round(score_avg_ms * 1e3, 3),
         "k_bytes_only": {"achieved": round(k_only, 1), "frac": round(k_only / HBM_PEAK_GBS, 4)},
         "topk_launch_avg_us": round(topk_avg_ms * 1e3, 3),
+        "topk_path": "score_hist + topk_hist (histogram from the score kernel)" if fused else "sampled cut",
     }
     result = {
         "metric": METRIC,

@@ -51,10 +51,11 @@
 extern "C" {
 #endif
 
-#define DSA_INDEXER_ABI_VERSION 4
+#define DSA_INDEXER_ABI_VERSION 5
 #define DSA_INDEXER_HEADS 32 /* indexer heads */
 #define DSA_INDEXER_DIM 64   /* head dimension */
 #define DSA_INDEXER_PAGE 64  /* c4 positions per page */
+#define DSA_INDEXER_HIST_BINS 2048 /* bins of the first-digit histogram (score_hist / topk_hist) */
 
 typedef enum {
   DSA_OK = 0,
@@ -106,6 +107,30 @@ int dsa_indexer_last_hip_error(void);
 int dsa_indexer_score(const void *q, const float *w, const void *k_pool, int64_t num_pages,
                       const int32_t *page_table, const int32_t *seq_lens, int32_t batch,
                       int32_t max_pages, float *logits, int32_t *row_hwm, hipStream_t stream);
+
+/*
+ * Score step that also counts what the top-k needs first (the fused pair
+ * dsa_indexer_score_hist + dsa_indexer_topk_hist; the top-k over the
+ * indexer's logits is the step page "The O(Actual) Indexer", section "The
+ * Benchmark Results", names as the remaining cost). Everything
+ * dsa_indexer_score does, argument for argument, and in addition:
+ *
+ *   hist       uint32 [batch][2048], 16-byte aligned. For every valid
+ *              position s < seq_lens[b] (clamped) the call adds one count to
+ *              hist[b][key(logits[b][s]) >> 21], where key() is the
+ *              order-preserving map of a float to 32 bits (non-negative x:
+ *              bits(x) | 0x80000000; negative x: ~bits(x); -0 counts as +0;
+ *              NaN as key 1, i.e. bin 0). The counts are added to what hist
+ *              holds: it must be all zero on entry (zero it once when it is
+ *              allocated; dsa_indexer_topk_hist sets it back to zero).
+ *
+ * Errors as for dsa_indexer_score (DSA_ERR_NULL also for a NULL hist,
+ * DSA_ERR_ALIGN for a misaligned one).
+ */
+int dsa_indexer_score_hist(const void *q, const float *w, const void *k_pool, int64_t num_pages,
+                           const int32_t *page_table, const int32_t *seq_lens, int32_t batch,
+                           int32_t max_pages, float *logits, int32_t *row_hwm, uint32_t *hist,
+                           hipStream_t stream);
 
 /*
  * Score step with fp8 keys (page "The Indexer O(max_context) Breakthrough"
@@ -194,6 +219,27 @@ size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k
 int dsa_indexer_topk(const float *logits, const int32_t *seq_lens, int32_t batch, int32_t max_c4,
                      int32_t k, int32_t *out_idx, float *out_vals, void *workspace,
                      size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Top-k step over logits written by dsa_indexer_score_hist, with its
+ * histogram: the same result as dsa_indexer_topk, argument for argument, plus
+ *
+ *   hist       uint32 [batch][2048], 16-byte aligned: the histogram that
+ *              dsa_indexer_score_hist accumulated for exactly these logits
+ *              and seq_lens. The call reads it and sets it back to all zero
+ *              (ready for the next dsa_indexer_score_hist).
+ *
+ * The histogram gives every row's first radix digit of the k-th largest
+ * score exactly, so no cut is sampled and the first radix pass is skipped:
+ * each segment keeps the keys in or above that bin. Counts that do not
+ * belong to these logits give unspecified positions (never accesses outside
+ * the buffers). Errors as for dsa_indexer_topk (DSA_ERR_NULL also for a NULL
+ * hist, DSA_ERR_ALIGN for a misaligned one); the workspace is sized by
+ * dsa_indexer_topk_workspace_bytes.
+ */
+int dsa_indexer_topk_hist(const float *logits, const int32_t *seq_lens, int32_t batch, int32_t max_c4,
+                          int32_t k, int32_t *out_idx, float *out_vals, uint32_t *hist, void *workspace,
+                          size_t ws_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Sparse attention over the selected positions (the step after the indexer;

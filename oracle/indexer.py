@@ -211,6 +211,43 @@ def topk_values(logits: np.ndarray, idx: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# First-digit histogram of the top-k's keys (the fused score + top-k pair)
+# ---------------------------------------------------------------------------
+#
+# The top-k after the indexer (page "The O(Actual) Indexer", section "The
+# Benchmark Results") ranks float32 scores. A radix select ranks them through
+# 32-bit keys whose unsigned order is that ranking, and the score step can
+# count the keys' first digit per request as it writes the logits. The
+# histogram is a plain count; only the key map needs care.
+
+def order_keys(x) -> np.ndarray:
+    """float32 scores -> uint32 keys whose unsigned order is the ranking of
+    ``topk``: a larger score has a larger key, -0 and +0 share a key, NaN is
+    the key 1 (below every number). IEEE-754 floats are sign-magnitude: for
+    x >= 0 the bits grow with x, so setting the sign bit puts them above every
+    negative; for x < 0 the bits grow as x falls, so their complement grows
+    with x and stays below 2^31."""
+    x = np.asarray(x, dtype=np.float32)
+    u = (x + np.float32(0.0)).view(np.uint32)  # -0 + 0 = +0
+    neg = (u >> np.uint32(31)) == 1
+    key = np.where(neg, ~u, u | np.uint32(0x80000000)).astype(np.uint32)
+    return np.where(np.isnan(x), np.uint32(1), key).astype(np.uint32)
+
+
+def key_histogram(logits, seq_lens, bits: int = 11) -> np.ndarray:
+    """uint32 [B, 2**bits]: for each request, how many of its positions
+    [0, L) have each value of the key's top ``bits`` bits."""
+    logits = np.asarray(logits, dtype=np.float32)
+    B, N = logits.shape
+    out = np.zeros((B, 1 << bits), dtype=np.uint32)
+    for b in range(B):
+        L = clamp_len(seq_lens[b], N)
+        digit = order_keys(logits[b, :L]) >> np.uint32(32 - bits)
+        out[b] = np.bincount(digit.astype(np.int64), minlength=1 << bits)
+    return out
+
+
+# ---------------------------------------------------------------------------
 # Several query tokens per request (multi-token prediction / speculative steps)
 # ---------------------------------------------------------------------------
 #

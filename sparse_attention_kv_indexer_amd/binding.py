@@ -14,6 +14,7 @@ import os
 from . import build as _build
 
 HEADS, DIM, PAGE = 32, 64, 64
+HIST_BINS = 2048  # first-digit histogram of score_hist / topk_hist
 ATT_HEADS, ATT_KD, ATT_VD = 32, 576, 512
 
 _STATUS = {0: "DSA_OK", -1: "DSA_ERR_NULL", -2: "DSA_ERR_SHAPE", -3: "DSA_ERR_ALIGN",
@@ -51,6 +52,10 @@ def load() -> ctypes.CDLL:
     lib.dsa_indexer_last_hip_error.argtypes = []
     lib.dsa_indexer_score.restype = ctypes.c_int
     lib.dsa_indexer_score.argtypes = [vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, vp]
+    lib.dsa_indexer_score_hist.restype = ctypes.c_int
+    lib.dsa_indexer_score_hist.argtypes = [vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, vp, vp]
+    lib.dsa_indexer_topk_hist.restype = ctypes.c_int
+    lib.dsa_indexer_topk_hist.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
     lib.dsa_indexer_score_fp8.restype = ctypes.c_int
     lib.dsa_indexer_score_fp8.argtypes = [vp, vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, vp]
     lib.dsa_indexer_score_mtp.restype = ctypes.c_int
@@ -128,6 +133,44 @@ def score(q, w, k_pool, page_table, seq_lens, out=None, row_hwm=None, stream=Non
         _stream_ptr(stream))
     if st != 0:
         raise DsaError(st, "dsa_indexer_score")
+    return out
+
+
+def hist_buffer(batch: int, device="cuda"):
+    """A zeroed first-digit histogram [batch, 2048] for score_hist / topk_hist
+    (int32 storage of the header's uint32 counts; topk_hist leaves it zero)."""
+    import torch
+
+    return torch.zeros((batch, HIST_BINS), dtype=torch.int32, device=device)
+
+
+def score_hist(q, w, k_pool, page_table, seq_lens, hist, out=None, row_hwm=None, stream=None):
+    """``score`` that also adds each request's first-digit key histogram to
+    ``hist`` (int32 [B, 2048], zero on entry; see the header)."""
+    import torch
+
+    B, S = page_table.shape
+    dev = q.device
+    bf16 = (torch.bfloat16, torch.int16)
+    _check(q, "q", bf16, (B, HEADS, DIM))
+    _check(w, "w", (torch.float32,), (B, HEADS), dev)
+    _check(k_pool, "k_pool", bf16, None, dev)
+    if k_pool.dim() != 3 or tuple(k_pool.shape[1:]) != (PAGE, DIM):
+        raise ValueError(f"k_pool has shape {tuple(k_pool.shape)}, expected [num_pages, {PAGE}, {DIM}]")
+    _check(page_table, "page_table", (torch.int32,), None, dev)
+    _check(seq_lens, "seq_lens", (torch.int32,), (B,), dev)
+    _check(hist, "hist", (torch.int32,), (B, HIST_BINS), dev)
+    if out is None:
+        out = torch.empty((B, S * PAGE), dtype=torch.float32, device=dev)
+    _check(out, "out", (torch.float32,), (B, S * PAGE), dev)
+    if row_hwm is not None:
+        _check(row_hwm, "row_hwm", (torch.int32,), (B,), dev)
+    st = load().dsa_indexer_score_hist(
+        q.data_ptr(), w.data_ptr(), k_pool.data_ptr(), k_pool.shape[0], page_table.data_ptr(),
+        seq_lens.data_ptr(), B, S, out.data_ptr(), row_hwm.data_ptr() if row_hwm is not None else None,
+        hist.data_ptr(), _stream_ptr(stream))
+    if st != 0:
+        raise DsaError(st, "dsa_indexer_score_hist")
     return out
 
 
@@ -211,9 +254,11 @@ _workspaces = {}  # (device, bytes) -> workspace reused by topk() calls that pas
 
 
 def topk(logits, seq_lens, k, out_idx=None, out_vals=None, with_values=False, workspace=None,
-         stream=None):
+         stream=None, hist=None):
     """Top-k positions [B, k] (int32, ascending, -1 padded) of each row, and
-    their scores [B, k] when ``with_values`` or ``out_vals`` is given."""
+    their scores [B, k] when ``with_values`` or ``out_vals`` is given. With
+    ``hist`` (the histogram score_hist filled for these logits) the call is
+    dsa_indexer_topk_hist, which also sets ``hist`` back to zero."""
     import torch
 
     B, N = logits.shape
@@ -237,9 +282,17 @@ def topk(logits, seq_lens, k, out_idx=None, out_vals=None, with_values=False, wo
         workspace = _workspaces[key]
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    vals_ptr = out_vals.data_ptr() if out_vals is not None else None
+    if hist is not None:
+        _check(hist, "hist", (torch.int32,), (B, HIST_BINS), dev)
+        st = load().dsa_indexer_topk_hist(logits.data_ptr(), seq_lens.data_ptr(), B, N, k, out_idx.data_ptr(),
+                                          vals_ptr, hist.data_ptr(), ws_ptr, ws_bytes, _stream_ptr(stream))
+        if st != 0:
+            raise DsaError(st, "dsa_indexer_topk_hist")
+        return out_idx, out_vals
     st = load().dsa_indexer_topk(
-        logits.data_ptr(), seq_lens.data_ptr(), B, N, k, out_idx.data_ptr(),
-        out_vals.data_ptr() if out_vals is not None else None, ws_ptr, ws_bytes, _stream_ptr(stream))
+        logits.data_ptr(), seq_lens.data_ptr(), B, N, k, out_idx.data_ptr(), vals_ptr, ws_ptr, ws_bytes,
+        _stream_ptr(stream))
     if st != 0:
         raise DsaError(st, "dsa_indexer_topk")
     return out_idx, out_vals

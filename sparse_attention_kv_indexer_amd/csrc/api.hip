@@ -55,7 +55,21 @@ int dsa_indexer_score(const void* q, const float* w, const void* k_pool, int64_t
       misaligned4(page_table) || misaligned4(seq_lens) || misaligned4(row_hwm))
     return DSA_ERR_ALIGN;
   return from_hip(dsa::launch_score(q, w, k_pool, nullptr, num_pages, page_table, seq_lens, batch, 1, max_pages,
-                                    logits, row_hwm, stream));
+                                    logits, row_hwm, nullptr, stream));
+}
+
+int dsa_indexer_score_hist(const void* q, const float* w, const void* k_pool, int64_t num_pages,
+                           const int32_t* page_table, const int32_t* seq_lens, int32_t batch, int32_t max_pages,
+                           float* logits, int32_t* row_hwm, uint32_t* hist, hipStream_t stream) {
+  if (!q || !w || !k_pool || !page_table || !seq_lens || !logits || !hist) return DSA_ERR_NULL;
+  if (batch < 1 || batch > kMaxBatch || max_pages < 1 || max_pages > kMaxPages || num_pages < 1 ||
+      (int64_t)batch * max_pages > kMaxSlots)
+    return DSA_ERR_SHAPE;
+  if (misaligned16(q) || misaligned16(w) || misaligned16(k_pool) || misaligned16(logits) || misaligned16(hist) ||
+      misaligned4(page_table) || misaligned4(seq_lens) || misaligned4(row_hwm))
+    return DSA_ERR_ALIGN;
+  return from_hip(dsa::launch_score(q, w, k_pool, nullptr, num_pages, page_table, seq_lens, batch, 1, max_pages,
+                                    logits, row_hwm, hist, stream));
 }
 
 int dsa_indexer_score_fp8(const void* q, const float* w, const void* k_pool_fp8, const float* k_scale,
@@ -69,7 +83,7 @@ int dsa_indexer_score_fp8(const void* q, const float* w, const void* k_pool_fp8,
       misaligned4(k_scale) || misaligned4(page_table) || misaligned4(seq_lens) || misaligned4(row_hwm))
     return DSA_ERR_ALIGN;
   return from_hip(dsa::launch_score(q, w, k_pool_fp8, k_scale, num_pages, page_table, seq_lens, batch, 1,
-                                    max_pages, logits, row_hwm, stream));
+                                    max_pages, logits, row_hwm, nullptr, stream));
 }
 
 int dsa_indexer_score_mtp(const void* q, const float* w, const void* k_pool, int64_t num_pages,
@@ -83,7 +97,7 @@ int dsa_indexer_score_mtp(const void* q, const float* w, const void* k_pool, int
       misaligned4(page_table) || misaligned4(seq_lens))
     return DSA_ERR_ALIGN;
   return from_hip(dsa::launch_score(q, w, k_pool, nullptr, num_pages, page_table, seq_lens, batch, tokens, max_pages,
-                                    logits, nullptr, stream));
+                                    logits, nullptr, nullptr, stream));
 }
 
 size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k) {
@@ -103,7 +117,23 @@ int dsa_indexer_topk(const float* logits, const int32_t* seq_lens, int32_t batch
   if (misaligned4(logits) || misaligned4(seq_lens) || misaligned4(out_idx) || misaligned4(out_vals) ||
       misaligned16(workspace))
     return DSA_ERR_ALIGN;
-  return from_hip(dsa::launch_topk(logits, seq_lens, batch, max_c4, k, out_idx, out_vals, workspace, stream));
+  return from_hip(
+      dsa::launch_topk(logits, seq_lens, batch, max_c4, k, out_idx, out_vals, workspace, nullptr, stream));
+}
+
+int dsa_indexer_topk_hist(const float* logits, const int32_t* seq_lens, int32_t batch, int32_t max_c4, int32_t k,
+                          int32_t* out_idx, float* out_vals, uint32_t* hist, void* workspace, size_t ws_bytes,
+                          hipStream_t stream) {
+  if (!logits || !seq_lens || !out_idx || !hist) return DSA_ERR_NULL;
+  if (batch < 1 || batch > kMaxBatch || max_c4 < 1 || max_c4 > dsa::kMaxRowPositions) return DSA_ERR_SHAPE;
+  if (k < 1 || k > max_c4) return DSA_ERR_K;
+  const size_t need = dsa_indexer_topk_workspace_bytes(batch, max_c4, k);
+  if (ws_bytes < need || (need > 0 && workspace == nullptr)) return DSA_ERR_WORKSPACE;
+  if (misaligned4(logits) || misaligned4(seq_lens) || misaligned4(out_idx) || misaligned4(out_vals) ||
+      misaligned16(workspace) || misaligned16(hist))
+    return DSA_ERR_ALIGN;
+  return from_hip(
+      dsa::launch_topk(logits, seq_lens, batch, max_c4, k, out_idx, out_vals, workspace, hist, stream));
 }
 
 size_t dsa_indexer_sparse_attention_workspace_bytes(int32_t batch, int32_t k) {

@@ -31,11 +31,32 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
                                            kRawBufferFlags);
 }
 
+// Monotone map float -> uint32 used by the top-k: a > b as floats (with -0 ==
+// +0) iff key(a) > key(b). Non-negative floats get the sign bit set, negative
+// ones are complemented; NaN maps to 1, below the key of every number (-inf
+// maps to 0x007FFFFF). Key 0 marks a slot past a row's length, so a key is
+// valid iff it is >= 1.
+__device__ __forceinline__ uint32_t order_key(float x) {
+  const uint32_t u = __float_as_uint(x + 0.0f);  // -0 + 0 = +0
+  const uint32_t key = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+  return (x != x) ? 1u : key;
+}
+
+// Histogram of the first digit of the keys (their top kHistBits bits), per
+// request: what the score kernel can count as it writes the logits, so that
+// the top-k needs neither a sampled cut nor its first radix pass.
+constexpr int kHistBits = 11;
+constexpr int kHistBins = 1 << kHistBits;
+constexpr int kHistShift = 32 - kHistBits;
+
 // Largest row width (positions) either kernel accepts: keeps every row's
 // byte range inside one 32-bit buffer range.
 constexpr int32_t kMaxRowPositions = 1 << 28;
 
 // Enqueue the score kernel (and, with row_hwm, the high-water-mark update).
+// hist: nullptr, or uint32 [B][kHistBins] to which the kernel adds, for every
+// valid position of request b, one count in bin order_key(score) >> kHistShift
+// (tokens == 1 only).
 // k_scale == nullptr: bfloat16 keys; otherwise e4m3fn keys with these per-key
 // scales (tokens == 1). tokens (1..4) query tokens per request: q [B][tokens][32][64],
 // w [B][tokens][32], seq_lens [B][tokens], logits [B][tokens][width];
@@ -43,14 +64,19 @@ constexpr int32_t kMaxRowPositions = 1 << 28;
 constexpr int32_t kMaxTokens = 4;
 hipError_t launch_score(const void* q, const float* w, const void* k_pool, const float* k_scale,
                         int64_t num_pages, const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
-                        int32_t tokens, int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream);
+                        int32_t tokens, int32_t max_pages, float* logits, int32_t* row_hwm, uint32_t* hist,
+                        hipStream_t stream);
 
 // 32-bit words of top-k workspace for these sizes.
 size_t topk_workspace_words(int32_t batch, int32_t max_c4);
 
-// Enqueue the top-k kernels (workspace: topk_workspace_words words, any contents).
+// Enqueue the top-k kernels (workspace: topk_workspace_words words, any
+// contents). hist: nullptr, or the score kernel's histograms of these logits,
+// which then replace the sampled cut and the first radix pass; the row kernel
+// sets every bin back to zero.
 hipError_t launch_topk(const float* logits, const int32_t* seq_lens, int32_t batch, int32_t max_c4,
-                       int32_t k, int32_t* out_idx, float* out_vals, void* workspace, hipStream_t stream);
+                       int32_t k, int32_t* out_idx, float* out_vals, void* workspace, uint32_t* hist,
+                       hipStream_t stream);
 
 // Sparse attention over the selected positions: 32 heads, 576-dim latents
 // (the first 512 dims are the value), at most kMaxAttK list entries per request.

@@ -188,7 +188,8 @@ void score_kernel(
     const int32_t* __restrict__ seq_lens,    // [B][kTok]
     int32_t batch, int32_t max_pages,
     float* __restrict__ logits,              // [B][kTok][max_pages * 64]
-    const int32_t* __restrict__ row_hwm)     // [B] or null (kTok == 1 only)
+    const int32_t* __restrict__ row_hwm,     // [B] or null (kTok == 1 only)
+    uint32_t* __restrict__ hist)             // [B][kHistBins] or null (kTok == 1 only)
 {
   const int lane = threadIdx.x;
   const int half = lane >> 5;
@@ -369,6 +370,26 @@ void score_kernel(
         const float v = base + lane >= len ? -__builtin_inff() : val[t];  // partial last page, shorter tokens
         const rsrc_t out = make_rsrc(logits + ((int64_t)bx * kTok + t) * sh.width + base, kPage * sizeof(float));
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), out, lane * 4, 0, 0);
+        if constexpr (kTok == 1 && !kFp8) {
+          if (hist != nullptr) {
+            // first-digit histogram of the page's valid scores: each distinct
+            // bin (a page's scores fall in a few dozen) is counted by the
+            // lowest of its lanes, then one atomic add per bin
+            const uint32_t bin = order_key(v) >> kHistShift;
+            uint64_t left = __ballot(base + lane < len);
+            uint32_t cnt = 0;
+            while (left != 0) {
+              const int l = __builtin_ctzll(left);
+              const uint32_t lb = (uint32_t)__builtin_amdgcn_readlane((int)bin, l);
+              const uint64_t same = __ballot(bin == lb) & left;
+              cnt = lane == l ? (uint32_t)__builtin_popcountll(same) : cnt;
+              left &= ~same;
+            }
+            if (cnt != 0)
+              __hip_atomic_fetch_add(hist + (int64_t)bx * kHistBins + bin, cnt, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
+          }
+        }
       }
     };
 
@@ -461,16 +482,17 @@ namespace {
 template <bool kFp8, int kTok>
 void launch_variant(int grid, hipStream_t stream, const void* q, const float* w, const void* k_pool,
                     const float* k_scale, int64_t num_pages, const int32_t* page_table, const int32_t* seq_lens,
-                    int32_t batch, int32_t max_pages, float* logits, int32_t* row_hwm) {
+                    int32_t batch, int32_t max_pages, float* logits, int32_t* row_hwm, uint32_t* hist) {
   hipLaunchKernelGGL((score_kernel<kFp8, kTok>), dim3(grid), dim3(64), 0, stream, static_cast<const uint16_t*>(q),
-                     w, k_pool, k_scale, num_pages, page_table, seq_lens, batch, max_pages, logits, row_hwm);
+                     w, k_pool, k_scale, num_pages, page_table, seq_lens, batch, max_pages, logits, row_hwm, hist);
 }
 
 }  // namespace
 
 hipError_t launch_score(const void* q, const float* w, const void* k_pool, const float* k_scale,
                         int64_t num_pages, const int32_t* page_table, const int32_t* seq_lens, int32_t batch,
-                        int32_t tokens, int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream) {
+                        int32_t tokens, int32_t max_pages, float* logits, int32_t* row_hwm, uint32_t* hist,
+                        hipStream_t stream) {
   // as many one-wave workgroups as stay resident, but no more than the largest
   // list these shapes allow (every slot a page, plus every tail chunk)
   const int64_t width = (int64_t)max_pages * kPage;
@@ -479,24 +501,24 @@ hipError_t launch_score(const void* q, const float* w, const void* k_pool, const
   const int grid = (int)std::min<int64_t>((int64_t)cu_count(stream) * per_cu, most);
   if (k_scale != nullptr) {
     launch_variant<true, 1>(grid, stream, q, w, k_pool, k_scale, num_pages, page_table, seq_lens, batch, max_pages,
-                            logits, row_hwm);
+                            logits, row_hwm, hist);
   } else {
     switch (tokens) {
       case 1:
         launch_variant<false, 1>(grid, stream, q, w, k_pool, k_scale, num_pages, page_table, seq_lens, batch,
-                                 max_pages, logits, row_hwm);
+                                 max_pages, logits, row_hwm, hist);
         break;
       case 2:
         launch_variant<false, 2>(grid, stream, q, w, k_pool, k_scale, num_pages, page_table, seq_lens, batch,
-                                 max_pages, logits, nullptr);
+                                 max_pages, logits, nullptr, nullptr);
         break;
       case 3:
         launch_variant<false, 3>(grid, stream, q, w, k_pool, k_scale, num_pages, page_table, seq_lens, batch,
-                                 max_pages, logits, nullptr);
+                                 max_pages, logits, nullptr, nullptr);
         break;
       default:
         launch_variant<false, 4>(grid, stream, q, w, k_pool, k_scale, num_pages, page_table, seq_lens, batch,
-                                 max_pages, logits, nullptr);
+                                 max_pages, logits, nullptr, nullptr);
         break;
     }
   }

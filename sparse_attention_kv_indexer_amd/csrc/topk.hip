@@ -65,17 +65,8 @@ constexpr int kSweep = 16 * kRowThreads;      // positions per block of the whol
 
 static_assert(kSegWaves * 64 == kSegThreads && kPerLane * kSegThreads == kSeg, "segment work split");
 static_assert(2 * kRowThreads * 4 == kSpecSlots * kSpec, "read-ahead: four 16-byte loads per lane");
+static_assert(kBins == kHistBins && kHistShift == 21, "the score kernel's histogram is the first radix digit");
 
-// Monotone map float -> uint32: a > b as floats (with -0 == +0) iff key(a) >
-// key(b). Non-negative floats get the sign bit set, negative ones are
-// complemented; NaN maps to 1, below the key of every number (-inf maps to
-// 0x007FFFFF). Key 0 marks a slot past the row's length, so a key is valid iff
-// it is >= 1.
-__device__ __forceinline__ uint32_t order_key(float x) {
-  const uint32_t u = __float_as_uint(x + 0.0f);  // -0 + 0 = +0
-  const uint32_t key = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
-  return (x != x) ? 1u : key;
-}
 // The float a key came from (+0 for either zero, a NaN for key 1).
 __device__ __forceinline__ uint32_t key_to_bits(uint32_t key) {
   return (key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key;
@@ -156,16 +147,20 @@ __device__ __forceinline__ void block_scan2(uint32_t& a, uint32_t& b, uint32_t* 
 struct Pick {
   uint32_t bin, above;
 };
-template <int kNB, typename RankOf>
-__device__ __forceinline__ Pick wave_pick(const uint32_t* hist, RankOf rank_of) {
+// load4(q, b) returns bins b .. b + 3 (b = the lane's lowest bin + 4 q).
+template <int kNB>
+__device__ __forceinline__ uint32_t pick_lo() {
+  return (uint32_t)(kNB - (kNB / 64) * ((threadIdx.x & 63) + 1));  // the lane's lowest bin
+}
+template <int kNB, typename Load4, typename RankOf>
+__device__ __forceinline__ Pick wave_pick(Load4 load4, RankOf rank_of) {
   constexpr int kPer = kNB / 64;    // bins per lane
   constexpr int kChunks = kPer / 4;
-  const int lane = threadIdx.x & 63;
-  const uint32_t lo = (uint32_t)(kNB - kPer * (lane + 1));  // the lane's lowest bin
+  const uint32_t lo = pick_lo<kNB>();
   uint32_t c[kPer];
 #pragma unroll
   for (int q = 0; q < kChunks; ++q) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(hist + hslot(lo + 4 * q));  // bins lo + 4q .. + 3
+    const u32x4 v = load4(q, lo + 4 * q);  // bins lo + 4q .. + 3
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const uint32_t x = v[e];
@@ -219,6 +214,32 @@ __device__ __forceinline__ Pick wave_pick(const uint32_t* hist, RankOf rank_of) 
   return Pick{(uint32_t)__builtin_amdgcn_readlane((int)bin, src), (uint32_t)__builtin_amdgcn_readlane((int)above, src)};
 }
 
+// wave_pick over a histogram in LDS (bins at hslot positions).
+template <int kNB, typename RankOf>
+__device__ __forceinline__ Pick wave_pick_lds(const uint32_t* hist, RankOf rank_of) {
+  return wave_pick<kNB>([&](int, uint32_t b) { return *reinterpret_cast<const u32x4*>(hist + hslot(b)); },
+                        rank_of);
+}
+
+// The score kernel's first-digit histogram of row b, loaded in wave_pick's
+// order (chunk q of the lane's bins); the loads are only issued here.
+struct HistRegs {
+  u32x4 c[kBins / 64 / 4];
+};
+__device__ __forceinline__ HistRegs load_row_hist(const uint32_t* hist, int b) {
+  const rsrc_t hr = make_rsrc(hist + (size_t)b * kHistBins, kHistBins * 4u);
+  const uint32_t lo = pick_lo<kBins>();
+  HistRegs h;
+#pragma unroll
+  for (int q = 0; q < kBins / 64 / 4; ++q)
+    h.c[q] = __builtin_amdgcn_raw_buffer_load_b128(hr, (lo + 4 * q) * 4, 0, 0);
+  return h;
+}
+// The bin of the k-th largest key of the row and the count above it.
+__device__ __forceinline__ Pick pick_row_hist(const HistRegs& h, int k) {
+  return wave_pick<kBins>([&](int q, uint32_t) { return h.c[q]; }, [&](uint32_t) { return (uint32_t)k; });
+}
+
 // Workspace layout (32-bit words), for B requests and n_seg segments per row:
 //   rec   [B][n_seg][kRecWords]           kept count of waves 0..3, cut key, unused
 //   pairs [B][n_seg][kSegWaves][kSub][2]  kept (key, position) of each wave, in position order
@@ -235,10 +256,15 @@ struct SegShared {
 };
 
 // One segment (seg) of request b's row of len positions (kSeg < len, k < len).
+// With the score kernel's histogram (hist != nullptr) the cut is exact: the
+// lower edge of the bin holding the row's k-th largest key, the same for every
+// segment of the row.
 __device__ __forceinline__ void process_segment(SegShared& sm, const float* __restrict__ logits, int b, int seg,
                                                 int len, int max_c4, int k, int n_seg, int batch,
-                                                uint32_t* __restrict__ ws) {
+                                                uint32_t* __restrict__ ws, const uint32_t* __restrict__ hist) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  HistRegs hr;
+  if (hist != nullptr) hr = load_row_hist(hist, b);  // in flight with the row's loads
   const int s0 = seg * kSeg;
   const float* row_ptr = logits + (int64_t)b * max_c4;
   // only positions [0, len) of the row are readable through this resource
@@ -276,7 +302,10 @@ __device__ __forceinline__ void process_segment(SegShared& sm, const float* __re
   const float want = 1.5f * (float)k * ((float)valid / (float)len) + 32.0f;
   const uint32_t share = want < (float)valid ? (uint32_t)want : (uint32_t)valid;
   uint32_t cut = 1u;  // keep every valid key
-  if (share < (uint32_t)valid) {
+  if (hist != nullptr) {
+    // (a total below k cannot come from the same logits; it keeps every key)
+    cut = max(pick_row_hist(hr, k).bin << 21, 1u);
+  } else if (share < (uint32_t)valid) {
     for (int i = tid; i < kBins; i += kSegThreads) sm.hist[i] = 0u;
     __syncthreads();
     const int ja = tid & (kPerLane - 1), jb = (tid + kPerLane / 2) & (kPerLane - 1);
@@ -290,7 +319,7 @@ __device__ __forceinline__ void process_segment(SegShared& sm, const float* __re
     if (kb != 0u) atomicAdd(&sm.hist[hslot(kb >> 21)], 1u);
     __syncthreads();
     // aim 25% (+4 samples) above the share among the samples
-    const Pick p = wave_pick<kBins>(sm.hist, [&](uint32_t n_s) {
+    const Pick p = wave_pick_lds<kBins>(sm.hist, [&](uint32_t n_s) {
       return (uint32_t)(1.25f * (float)share * ((float)n_s / (float)valid)) + 4u; });
     cut = max(p.bin << 21, 1u);
   }
@@ -325,13 +354,14 @@ __device__ __forceinline__ void process_segment(SegShared& sm, const float* __re
 __global__ __launch_bounds__(kSegThreads) void topk_segment_kernel(const float* __restrict__ logits,
                                                                     const int32_t* __restrict__ seq_lens,
                                                                     int32_t max_c4, int32_t k, int32_t n_seg,
-                                                                    uint32_t* __restrict__ ws) {
+                                                                    uint32_t* __restrict__ ws,
+                                                                    const uint32_t* __restrict__ hist) {
   __shared__ SegShared sm;
   const int b = blockIdx.x;
   const int len = min(max(seq_lens[b], 0), max_c4);
   if (len <= kSeg || len <= k) return;  // the row kernel handles such a row alone
   for (int seg = blockIdx.y; seg * kSeg < len; seg += gridDim.y) {
-    process_segment(sm, logits, b, seg, len, max_c4, k, n_seg, (int)gridDim.x, ws);
+    process_segment(sm, logits, b, seg, len, max_c4, k, n_seg, (int)gridDim.x, ws, hist);
     __syncthreads();  // sm is reused by the next segment
   }
 }
@@ -353,6 +383,7 @@ struct RowShared {
   uint32_t roff[kRound];  //   its first pair not read ahead, in the round's list of those
   uint32_t part[2 * kRowWaves];
   uint32_t bcast[2];
+  uint32_t hpick[2];  // from the score kernel's histogram: bin of the k-th largest, count above it
   uint32_t max_cut;
 };
 __shared__ RowShared rs;
@@ -383,7 +414,7 @@ __device__ __forceinline__ void radix_pass(uint32_t& T, uint32_t& mask, uint32_t
   count(h, shift, dmask);
   __syncthreads();
   if ((threadIdx.x >> 6) == 0) {
-    const Pick p = wave_pick<(kPass == 2 ? kBins / 2 : kBins)>(h, [&](uint32_t) { return remaining; });
+    const Pick p = wave_pick_lds<(kPass == 2 ? kBins / 2 : kBins)>(h, [&](uint32_t) { return remaining; });
     if (threadIdx.x == 0) {
       rs.bcast[0] = p.bin;
       rs.bcast[1] = p.above;
@@ -398,13 +429,16 @@ __device__ __forceinline__ void radix_pass(uint32_t& T, uint32_t& mask, uint32_t
 
 // Exact radix select over the n candidates in LDS (n >= k): the k-th largest
 // key T and r, the number of keys == T taken. The histograms are clear on
-// entry.
+// entry. With from_hist, the first digit (bin0) and the count of keys in
+// higher bins (above0) are known already and the first pass is skipped.
 struct Kth {
   uint32_t T, r;
 };
-__device__ __forceinline__ Kth select_candidates(int n, int k) {
+__device__ __forceinline__ Kth select_candidates(int n, int k, bool from_hist, uint32_t bin0, uint32_t above0) {
   const int tid = threadIdx.x;
-  uint32_t T = 0u, mask = 0u, remaining = (uint32_t)k;
+  uint32_t T = from_hist ? bin0 << 21 : 0u;
+  uint32_t mask = from_hist ? 0xFFE00000u : 0u;
+  uint32_t remaining = (uint32_t)k - (from_hist ? above0 : 0u);
   auto count = [&](uint32_t* h, int shift, uint32_t dmask) {
     int i = tid;
     for (; i + 3 * kRowThreads < n; i += 4 * kRowThreads) {
@@ -420,7 +454,7 @@ __device__ __forceinline__ Kth select_candidates(int n, int k) {
       if ((kk & mask) == T) atomicAdd(&h[hslot((kk >> shift) & dmask)], 1u);
     }
   };
-  radix_pass<0>(T, mask, remaining, count);
+  if (!from_hist) radix_pass<0>(T, mask, remaining, count);
   radix_pass<1>(T, mask, remaining, count);
   radix_pass<2>(T, mask, remaining, count);
   return Kth{T, remaining};
@@ -616,8 +650,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
                                                                 int32_t max_c4, int32_t k,
                                                                 int32_t* __restrict__ out_idx,
                                                                 float* __restrict__ out_vals,
-                                                                const uint32_t* __restrict__ ws, int32_t n_seg) {
+                                                                const uint32_t* __restrict__ ws, int32_t n_seg,
+                                                                uint32_t* __restrict__ hist) {
   const int b = blockIdx.x, tid = threadIdx.x;
+  // this row's histogram, set back to zero for the next score call once read
+  const rsrc_t hrow = make_rsrc(hist != nullptr ? hist + (size_t)b * kHistBins : nullptr,
+                                hist != nullptr ? kHistBins * 4u : 0u);
+  static_assert(kHistBins == 2 * kRowThreads, "two bins per lane");
+  auto clear_hist_row = [&]() { store_pair(hrow, tid, 0u, 0u); };
   const int len = min(max(seq_lens[b], 0), max_c4);
   const float* row_ptr = logits + (int64_t)b * max_c4;
   // only positions [0, len) of the row are readable through this resource
@@ -629,6 +669,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
 
   if (len <= k) {
     // every valid position is chosen
+    if (hist != nullptr) clear_hist_row();
     for (int i = tid; i < k; i += kRowThreads) {
       store_b32(oi, i, i < len ? (uint32_t)i : 0xFFFFFFFFu);
       if (with_vals) store_b32(ov, i, i < len ? load_b32(row, i) : 0x7FC00000u);
@@ -636,6 +677,13 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     return;
   }
 
+  if (hist != nullptr && tid < 64) {
+    const Pick p = pick_row_hist(load_row_hist(hist, b), k);
+    if (tid == 0) {
+      rs.hpick[0] = p.bin;
+      rs.hpick[1] = p.above;
+    }
+  }
   clear_hists();
   int n;
   if (len <= kSeg) {
@@ -656,8 +704,15 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     n = gather_segments(ws, b, (int)gridDim.x, n_seg, len);
   }
   __syncthreads();
+  const bool from_hist = hist != nullptr;
+  uint32_t bin0 = 0u, above0 = 0u;
+  if (from_hist) {
+    bin0 = rs.hpick[0];
+    above0 = rs.hpick[1];
+    clear_hist_row();  // wave 0 read it before the barrier
+  }
   if (n >= k) {  // n < 0: more than kCap candidates
-    const Kth t = select_candidates(n, k);
+    const Kth t = select_candidates(n, k, from_hist, bin0, above0);
     // every key a segment left out lies below its cut, hence below T
     if (t.T >= rs.max_cut) {
       write_from_candidates(n, t, oi, ov, with_vals);
@@ -679,15 +734,16 @@ size_t topk_workspace_words(int32_t batch, int32_t max_c4) {
 }
 
 hipError_t launch_topk(const float* logits, const int32_t* seq_lens, int32_t batch, int32_t max_c4,
-                       int32_t k, int32_t* out_idx, float* out_vals, void* workspace, hipStream_t stream) {
+                       int32_t k, int32_t* out_idx, float* out_vals, void* workspace, uint32_t* hist,
+                       hipStream_t stream) {
   const int n_seg = (int)(((int64_t)max_c4 + kSeg - 1) / kSeg);
   uint32_t* ws = static_cast<uint32_t*>(workspace);
   // a row reaches the segment kernel only if it is longer than kSeg and than k
   if (max_c4 > kSeg && k < max_c4)
     hipLaunchKernelGGL(topk_segment_kernel, dim3(batch, min(n_seg, 65535)), dim3(kSegThreads), 0, stream, logits, seq_lens,
-                       max_c4, k, n_seg, ws);
+                       max_c4, k, n_seg, ws, hist);
   hipLaunchKernelGGL(topk_row_kernel, dim3(batch), dim3(kRowThreads), 0, stream, logits, seq_lens, max_c4, k,
-                     out_idx, out_vals, ws, n_seg);
+                     out_idx, out_vals, ws, n_seg, hist);
   return hipGetLastError();
 }
 

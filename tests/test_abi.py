@@ -29,13 +29,13 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for name in names:
         assert hasattr(lib, name), f"{name} not exported"
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dsa_indexer_abi_version() == 4
+    assert lib.dsa_indexer_abi_version() == 5
     for st in (OK, NULL, SHAPE, ALIGN, K, WS, -6):
         assert lib.dsa_indexer_status_string(st).decode() not in ("", "unknown status")
     assert lib.dsa_indexer_status_string(12345).decode() == "unknown status"
@@ -98,6 +98,40 @@ def test_topk_workspace_contract(lib):
     assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=32768, k=2048, workspace=A, ws_bytes=need - 1)) == WS
     assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=32768, k=2048, workspace=None, ws_bytes=need)) == WS
     assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=32768, k=2048, workspace=A + 4, ws_bytes=need)) == ALIGN
+
+
+def score_hist_args(**over):
+    args = dict(q=A, w=A, k_pool=A, num_pages=4, page_table=A, seq_lens=A, batch=2, max_pages=3,
+                logits=A, row_hwm=None, hist=A, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("field", ["q", "w", "k_pool", "page_table", "seq_lens", "logits", "hist"])
+def test_score_hist_null(lib, field):
+    assert lib.dsa_indexer_score_hist(*score_hist_args(**{field: None})) == NULL
+
+
+@pytest.mark.parametrize("over,want", [(dict(batch=0), SHAPE), (dict(max_pages=0), SHAPE), (dict(num_pages=0), SHAPE),
+                                       (dict(hist=A + 8), ALIGN), (dict(q=A + 8), ALIGN), (dict(row_hwm=A + 2), ALIGN)])
+def test_score_hist_rejects(lib, over, want):
+    assert lib.dsa_indexer_score_hist(*score_hist_args(**over)) == want
+
+
+def topk_hist_args(**over):
+    args = dict(logits=A, seq_lens=A, batch=2, max_c4=128, k=16, out_idx=A, out_vals=None, hist=A,
+                workspace=A, ws_bytes=1 << 30, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("over,want", [(dict(logits=None), NULL), (dict(hist=None), NULL), (dict(out_idx=None), NULL),
+                                       (dict(batch=0), SHAPE), (dict(k=0), K), (dict(k=129), K),
+                                       (dict(hist=A + 4), ALIGN), (dict(out_idx=A + 2), ALIGN),
+                                       (dict(batch=64, max_c4=32768, k=2048, ws_bytes=64 * 8 * (8 + 2 * 4096) * 4 - 1),
+                                        WS)])
+def test_topk_hist_rejects(lib, over, want):
+    assert lib.dsa_indexer_topk_hist(*topk_hist_args(**over)) == want
 
 
 def score_fp8_args(**over):
