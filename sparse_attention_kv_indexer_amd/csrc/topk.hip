@@ -62,6 +62,10 @@ constexpr int kRound = 256;                   // sub-slot records per gather rou
 constexpr int kSpecSlots = 32;                // sub-slots read before their counts are known
 constexpr int kSpec = 256;                    // pairs read ahead per such sub-slot
 constexpr int kSweep = 16 * kRowThreads;      // positions per block of the whole-row output sweep
+// Rows of at least this many segments select over the candidates' own key
+// range (measured on rows of 32768 positions: the top-k 1.7 us faster; on
+// rows of six or seven segments it was slower, so they keep the key's digits).
+constexpr int kRangedMinSegs = 8;
 
 static_assert(kSegWaves * 64 == kSegThreads && kPerLane * kSegThreads == kSeg, "segment work split");
 static_assert(2 * kRowThreads * 4 == kSpecSlots * kSpec, "read-ahead: four 16-byte loads per lane");
@@ -384,6 +388,7 @@ struct RowShared {
   uint32_t part[2 * kRowWaves];
   uint32_t bcast[2];
   uint32_t hpick[2];  // from the score kernel's histogram: bin of the k-th largest, count above it
+  uint32_t range[2];  // smallest and largest candidate key
   uint32_t max_cut;
 };
 __shared__ RowShared rs;
@@ -395,7 +400,11 @@ __device__ __forceinline__ uint32_t* pass_hist(int pass) {
 // Clears the three histograms and max_cut (a barrier must follow before
 // they are counted into).
 __device__ __forceinline__ void clear_hists() {
-  if (threadIdx.x == 0) rs.max_cut = 0u;
+  if (threadIdx.x == 0) {
+    rs.max_cut = 0u;
+    rs.range[0] = 0xFFFFFFFFu;
+    rs.range[1] = 0u;
+  }
   for (int i = threadIdx.x; i < kBins; i += kRowThreads) {
     rs.hist0[i] = 0u;
     rs.hist1[i] = 0u;
@@ -458,6 +467,70 @@ __device__ __forceinline__ Kth select_candidates(int n, int k, bool from_hist, u
   radix_pass<1>(T, mask, remaining, count);
   radix_pass<2>(T, mask, remaining, count);
   return Kth{T, remaining};
+}
+
+// Exact radix select over the n candidates in LDS (n >= k) on the offsets
+// key - base from the smallest candidate key: the digits (11, 11, then at
+// most 10 bits) start at the top bit of the candidates' key range, so that
+// candidates gathered above the segments' cuts, which share a few bins of the
+// key's own first digit, spread over up to 2048 bins. Out of line, like the
+// whole-row path, so that the common path's code stays as it is. The
+// histograms are clear and rs.range is (~0, 0) on entry.
+__device__ __noinline__ Kth select_candidates_ranged(int n, int k) {
+  const int tid = threadIdx.x;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  for (int i = tid; i < n; i += kRowThreads) {
+    const uint32_t kk = rs.cand_key[i];
+    lo = min(lo, kk);
+    hi = max(hi, kk);
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
+  }
+  if ((tid & 63) == 0) {
+    atomicMin(&rs.range[0], lo);
+    atomicMax(&rs.range[1], hi);
+  }
+  __syncthreads();
+  const uint32_t base = rs.range[0];
+  const uint32_t span = rs.range[1] - base;
+  int top = span == 0u ? 0 : 32 - __builtin_clz(span);  // bits of the offsets still to resolve
+  uint32_t prefix = 0u, remaining = (uint32_t)k;
+  for (int pass = 0; top > 0; ++pass) {  // at most three passes (11 + 11 + 10 bits)
+    const int low = max(top - 11, 0), width = top - low;
+    const uint32_t dmask = (1u << width) - 1u;
+    uint32_t* h = pass_hist(pass);
+    int i = tid;
+    for (; i + 3 * kRowThreads < n; i += 4 * kRowThreads) {
+      uint32_t off[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) off[u] = rs.cand_key[i + u * kRowThreads] - base;
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        if ((uint32_t)((uint64_t)off[u] >> top) == prefix) atomicAdd(&h[hslot((off[u] >> low) & dmask)], 1u);
+    }
+    for (; i < n; i += kRowThreads) {
+      const uint32_t off = rs.cand_key[i] - base;
+      if ((uint32_t)((uint64_t)off >> top) == prefix) atomicAdd(&h[hslot((off >> low) & dmask)], 1u);
+    }
+    __syncthreads();
+    if ((tid >> 6) == 0) {
+      const Pick p = pass < 2 ? wave_pick_lds<kBins>(h, [&](uint32_t) { return remaining; })
+                              : wave_pick_lds<kBins / 2>(h, [&](uint32_t) { return remaining; });
+      if (tid == 0) {
+        rs.bcast[0] = p.bin;
+        rs.bcast[1] = p.above;
+      }
+    }
+    __syncthreads();
+    prefix = (prefix << width) | rs.bcast[0];
+    remaining -= rs.bcast[1];
+    top = low;
+    // (bcast is written again only after the next pass's first barrier)
+  }
+  return Kth{base + prefix, remaining};
 }
 
 // Writes the chosen positions from the n candidates in LDS (position order);
@@ -712,7 +785,9 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     clear_hist_row();  // wave 0 read it before the barrier
   }
   if (n >= k) {  // n < 0: more than kCap candidates
-    const Kth t = select_candidates(n, k, from_hist, bin0, above0);
+    // a long row's candidates lie above high cuts, in a narrow key range
+    const Kth t = (!from_hist && len >= kRangedMinSegs * kSeg) ? select_candidates_ranged(n, k)
+                                                                : select_candidates(n, k, from_hist, bin0, above0);
     // every key a segment left out lies below its cut, hence below T
     if (t.T >= rs.max_cut) {
       write_from_candidates(n, t, oi, ov, with_vals);

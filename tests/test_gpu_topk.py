@@ -180,3 +180,26 @@ def test_too_few_candidates_falls_back(lib):
     xd, ld = _upload(x, lens)
     idx, vals = run_topk(lib, xd, ld, k)
     check_topk_exact(idx, vals, x, lens, k)
+
+
+def test_long_rows_with_narrow_candidate_ranges(lib):
+    """Rows of at least eight segments select over the candidates' own key
+    range: candidates that are all one value (no digit left to resolve),
+    two values one ulp apart, and ordinary random rows, with k around the
+    number of top values."""
+    rng = np.random.default_rng(12)
+    B, N, k = 6, 32768, 2048
+    x = -np.abs(rng.standard_normal((B, N))).astype(np.float32) - 1.0  # everything below -1
+    top = rng.permutation(N)[:2500]
+    x[0, top] = 5.0                                   # 2500 equal top scores
+    x[1, top[:1000]] = np.float32(5.0)
+    x[1, top[1000:]] = np.nextafter(np.float32(5.0), np.float32(0))  # one ulp apart
+    x[2, top[:2048]] = 3.0                            # exactly k top scores
+    x[3] = rng.standard_normal(N).astype(np.float32)
+    x[4] = rng.standard_normal(N).astype(np.float32) * np.float32(1e-3) + 7.0  # narrow range of all keys
+    x[5, top] = rng.integers(0, 4, size=top.size).astype(np.float32) + 10.0  # ties among few top values
+    lens = np.array([N, N, N, 24000, 30001, N])
+    say("topk long rows, narrow candidate ranges")
+    xd, ld = _upload(x, lens)
+    idx, vals = run_topk(lib, xd, ld, k)
+    check_topk_exact(idx, vals, x, lens, k)
