@@ -7,14 +7,18 @@
 // and -inf at every position at or past the length, over a row of
 // max_pages * 64 positions.
 //
-// Work list. The work of one call is a flat list: first every valid page of
-// every request (request-major, page-minor), then the -inf tail of every
+// Work lists. The work of one call is two flat lists: every valid page of
+// every request (request-major, page-minor), and the -inf tail of every
 // request cut into chunks of kTailChunk positions. The tail of a request runs
 // from its first page past the length to the row end (stateless mode) or to
 // the page holding its previous high-water mark (incremental mode, where
 // everything beyond is -inf already). A fixed grid of one-wave workgroups, as
 // many as the chip keeps resident (capped by the largest list the shapes
-// allow), splits the list into equal contiguous ranges. The launch shape
+// allow), splits each list into equal contiguous ranges when every
+// workgroup gets pages (a workgroup scores its pages, then writes its tail
+// chunks: writes between the page reads slow the read stream), and splits the
+// two lists as one otherwise (the workgroups past the pages take the tail).
+// The launch shape
 // depends only on (batch, max_pages), so it can be captured once and replayed
 // for any lengths, and the work and HBM traffic follow the actual lengths:
 // pages past a length are never read (the early exit of the section "The
@@ -198,17 +202,34 @@ void score_kernel(
                  make_rsrc(row_hwm != nullptr ? row_hwm : seq_lens, (uint32_t)batch * 4u),
                  kTok == 1 && row_hwm != nullptr, batch, max_pages * kPage, kTok};
 
-  // list totals, then this workgroup's contiguous range [s, e)
+  // list totals, then this workgroup's contiguous ranges: pages [s, pe) and
+  // tail chunks [ts, te)
   uint32_t n_pages = 0, n_chunks = 0;
   for (int b0 = 0; b0 < batch; b0 += 64) {
     const RowWork r = row_work(sh, b0 + lane);
     n_pages += wave_total(r.pages);
     n_chunks += wave_total(r.chunks);
   }
-  const uint32_t total = n_pages + n_chunks;
-  const uint32_t per = (total + gridDim.x - 1) / gridDim.x;
-  const uint32_t s = blockIdx.x * per, e = min(total, s + per);
-  if (s >= e) return;
+  uint32_t s, pe, ts, te;
+  if (n_pages >= gridDim.x) {
+    // every workgroup has pages: each list split on its own, tail after pages
+    const uint32_t per_p = (n_pages + gridDim.x - 1) / gridDim.x;
+    s = min(n_pages, blockIdx.x * per_p);
+    pe = min(n_pages, s + per_p);
+    const uint32_t per_t = (n_chunks + gridDim.x - 1) / gridDim.x;
+    ts = min(n_chunks, blockIdx.x * per_t);
+    te = min(n_chunks, ts + per_t);
+  } else {
+    // fewer pages than workgroups: one list, pages then tail chunks, so that
+    // the workgroups without pages take the tail
+    const uint32_t total = n_pages + n_chunks, per = (total + gridDim.x - 1) / gridDim.x;
+    const uint32_t a = min(total, blockIdx.x * per), z = min(total, a + per);
+    s = min(a, n_pages);
+    pe = min(z, n_pages);
+    ts = max(a, n_pages) - n_pages;
+    te = max(z, n_pages) - n_pages;
+  }
+  if (s >= pe && ts >= te) return;
 
   using Fmt = KeyFormat<kFp8>;
   using Regs = PageRegs<kFp8>;
@@ -246,8 +267,7 @@ void score_kernel(
     stash_n = 0;
   };
 
-  if (s < n_pages) {
-    const uint32_t pe = min(e, n_pages);
+  if (s < pe) {
     Window W{0, 0, 0, 0, 0};
     window_load(W, sh, false);
 
@@ -469,15 +489,15 @@ void score_kernel(
     }
   }
 
-  if (e > n_pages) {
+  if (ts < te) {
     // -inf tail chunks
     Window W{0, 0, 0, 0, 0};
     window_load(W, sh, true);
     const u32x4 ninf = {0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u};
-    for (uint32_t it = max(s, n_pages); it < e; ++it) {
+    for (uint32_t it = ts; it < te; ++it) {
       int b;
       uint32_t c;
-      window_find(W, it - n_pages, sh, true, b, c);
+      window_find(W, it, sh, true, b, c);
       const RowWork r = row_work(sh, b);
       const uint32_t c0 = r.tail0 + c * kTailChunk, c1 = min(r.tail1, c0 + kTailChunk);
 #pragma unroll
