@@ -235,15 +235,17 @@ void score_kernel(
   using Regs = PageRegs<kFp8>;
   __shared__ u32x4 tile[kPageChunks];  // one bf16 page, or the first half for fp8
 
-  // bf16 keys, one query token: a page's 64 scores go to an LDS stash,
+  // bf16 keys: a page's 64 scores (per query token) go to an LDS stash,
   // written out as runs of contiguous logits at the end of the workgroup's
   // pages (or when the stash is full) with 1 KiB wave stores. Measured with
   // a load probe over random 8 KiB pages: 256 B of results stored after every
   // page cost the read stream 6 us of 48 at 32768 pages; the same bytes
-  // written in one burst per workgroup cost 2. (fp8 pages measured no gain.)
-  constexpr bool kStashed = kTok == 1 && !kFp8;
-  constexpr int kStash = 16;  // pages
-  __shared__ __attribute__((aligned(16))) uint32_t stash[kStashed ? kStash * kPage : 4];
+  // written in one burst per workgroup cost 2. (Measured in the kernel: full
+  // 50.2 -> 48.4 us; two and three query tokens 1-2 us per step faster; fp8
+  // pages and four query tokens no gain, so they store per page.)
+  constexpr bool kStashed = !kFp8 && kTok <= 3;
+  constexpr int kStash = kTok == 1 ? 16 : 8;  // pages; token t's rows at [t][page][64]
+  __shared__ __attribute__((aligned(16))) uint32_t stash[kStashed ? kTok * kStash * kPage : 4];
   __shared__ int stash_b[kStash], stash_j[kStash];
   int stash_n = 0;
   auto stash_flush = [&]() {
@@ -257,10 +259,14 @@ void score_kernel(
       while (q < stash_n && stash_b[q] == rb && stash_j[q] == rj + (q - p)) ++q;
       q = __builtin_amdgcn_readfirstlane(q);
       const int words = (q - p) * kPage;
-      const rsrc_t out = make_rsrc(logits + (int64_t)rb * sh.width + (int64_t)rj * kPage, (uint32_t)words * 4u);
-      for (int w0 = lane * 4; w0 < words; w0 += 256)
-        __builtin_amdgcn_raw_buffer_store_b128(*reinterpret_cast<const u32x4*>(&stash[p * kPage + w0]), out, w0 * 4, 0,
-                                               0);
+#pragma unroll
+      for (int t = 0; t < kTok; ++t) {
+        const rsrc_t out = make_rsrc(logits + ((int64_t)rb * kTok + t) * sh.width + (int64_t)rj * kPage,
+                                     (uint32_t)words * 4u);
+        for (int w0 = lane * 4; w0 < words; w0 += 256)
+          __builtin_amdgcn_raw_buffer_store_b128(
+              *reinterpret_cast<const u32x4*>(&stash[(t * kStash + p) * kPage + w0]), out, w0 * 4, 0, 0);
+      }
       p = q;
     }
     __syncthreads();  // the stash is rewritten next
@@ -417,18 +423,19 @@ void score_kernel(
           val[t] = half ? p1 : p0;
         }
       }
+      if constexpr (kStashed) {
+        if (stash_n == kStash) stash_flush();
+        if (lane == 0) {
+          stash_b[stash_n] = bx;
+          stash_j[stash_n] = (int)jx;
+        }
+      }
 #pragma unroll
       for (int t = 0; t < kTok; ++t) {
         const int len = clamp_len(seq_lens[bx * kTok + t], sh.width);
         const float v = base + lane >= len ? -__builtin_inff() : val[t];  // partial last page, shorter tokens
         if constexpr (kStashed) {
-          if (stash_n == kStash) stash_flush();
-          stash[stash_n * kPage + lane] = __builtin_bit_cast(uint32_t, v);
-          if (lane == 0) {
-            stash_b[stash_n] = bx;
-            stash_j[stash_n] = (int)jx;
-          }
-          ++stash_n;
+          stash[(t * kStash + stash_n) * kPage + lane] = __builtin_bit_cast(uint32_t, v);
         } else {
           const rsrc_t out = make_rsrc(logits + ((int64_t)bx * kTok + t) * sh.width + base, kPage * sizeof(float));
           __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), out, lane * 4, 0, 0);
@@ -454,6 +461,7 @@ void score_kernel(
           }
         }
       }
+      if constexpr (kStashed) ++stash_n;
     };
 
     // state at the top of each half of the loop, for the item `it` it computes:
