@@ -62,10 +62,6 @@ constexpr int kRound = 256;                   // sub-slot records per gather rou
 constexpr int kSpecSlots = 32;                // sub-slots read before their counts are known
 constexpr int kSpec = 256;                    // pairs read ahead per such sub-slot
 constexpr int kSweep = 16 * kRowThreads;      // positions per block of the whole-row output sweep
-// Rows of at least this many segments select over the candidates' own key
-// range (measured on rows of 32768 positions: the top-k 1.7 us faster; on
-// rows of six or seven segments it was slower, so they keep the key's digits).
-constexpr int kRangedMinSegs = 8;
 
 static_assert(kSegWaves * 64 == kSegThreads && kPerLane * kSegThreads == kSeg, "segment work split");
 static_assert(2 * kRowThreads * 4 == kSpecSlots * kSpec, "read-ahead: four 16-byte loads per lane");
@@ -111,6 +107,18 @@ __device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t v) {
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);  // row_bcast:15
   v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);  // row_bcast:31
   return v;
+}
+
+// The largest value over the 64 lanes of a wave, in every lane: the same DPP
+// steps as the scan with max (0 is neutral), then lane 63's value.
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false));  // row_shr:1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false));  // row_shr:2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false));  // row_shr:4
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false));  // row_shr:8
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
 // Inclusive scans of a and b over the workgroup's lanes in lane order, and
@@ -388,7 +396,7 @@ struct RowShared {
   uint32_t part[2 * kRowWaves];
   uint32_t bcast[2];
   uint32_t hpick[2];  // from the score kernel's histogram: bin of the k-th largest, count above it
-  uint32_t range[2];  // smallest and largest candidate key
+  uint32_t range[2];  // candidates at or above the largest cut, largest candidate key
   uint32_t max_cut;
 };
 __shared__ RowShared rs;
@@ -402,7 +410,7 @@ __device__ __forceinline__ uint32_t* pass_hist(int pass) {
 __device__ __forceinline__ void clear_hists() {
   if (threadIdx.x == 0) {
     rs.max_cut = 0u;
-    rs.range[0] = 0xFFFFFFFFu;
+    rs.range[0] = 0u;
     rs.range[1] = 0u;
   }
   for (int i = threadIdx.x; i < kBins; i += kRowThreads) {
@@ -469,32 +477,33 @@ __device__ __forceinline__ Kth select_candidates(int n, int k, bool from_hist, u
   return Kth{T, remaining};
 }
 
-// Exact radix select over the n candidates in LDS (n >= k) on the offsets
-// key - base from the smallest candidate key: the digits (11, 11, then at
-// most 10 bits) start at the top bit of the candidates' key range, so that
-// candidates gathered above the segments' cuts, which share a few bins of the
-// key's own first digit, spread over up to 2048 bins. Out of line, like the
-// whole-row path, so that the common path's code stays as it is. The
-// histograms are clear and rs.range is (~0, 0) on entry.
-__device__ __noinline__ Kth select_candidates_ranged(int n, int k) {
+// Exact radix select over the candidates in LDS at or above base, the
+// largest segment cut. The candidates hold the whole top k exactly when its
+// k-th largest key T is >= base, so keys below base never decide T: the
+// digits (11, 11, then at most 10 bits) are those of the offset key - base,
+// starting at the top bit of the range [base, largest key]. That range is
+// narrow (the candidates above a cut share a few bins of the key's own first
+// digit, where the first pass would pile its LDS atomics onto a few words).
+// Returns r = 0xFFFFFFFF if fewer than k keys reach base (T < base: the caller
+// selects over the whole row). Out of line, like the whole-row path, so that
+// the common path's code stays as it is. The histograms are clear and
+// rs.range is (0, 0) on entry.
+__device__ __noinline__ Kth select_candidates_ranged(int n, int k, uint32_t base) {
   const int tid = threadIdx.x;
-  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+  uint32_t hi = 0u, above = 0u;
   for (int i = tid; i < n; i += kRowThreads) {
     const uint32_t kk = rs.cand_key[i];
-    lo = min(lo, kk);
     hi = max(hi, kk);
+    above += kk >= base ? 1u : 0u;
   }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    lo = min(lo, (uint32_t)__shfl_xor((int)lo, o));
-    hi = max(hi, (uint32_t)__shfl_xor((int)hi, o));
-  }
+  hi = wave_max(hi);
+  above = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(above), 63);
   if ((tid & 63) == 0) {
-    atomicMin(&rs.range[0], lo);
+    atomicAdd(&rs.range[0], above);
     atomicMax(&rs.range[1], hi);
   }
   __syncthreads();
-  const uint32_t base = rs.range[0];
+  if (rs.range[0] < (uint32_t)k) return Kth{0u, 0xFFFFFFFFu};
   const uint32_t span = rs.range[1] - base;
   int top = span == 0u ? 0 : 32 - __builtin_clz(span);  // bits of the offsets still to resolve
   uint32_t prefix = 0u, remaining = (uint32_t)k;
@@ -506,14 +515,16 @@ __device__ __noinline__ Kth select_candidates_ranged(int n, int k) {
     for (; i + 3 * kRowThreads < n; i += 4 * kRowThreads) {
       uint32_t off[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) off[u] = rs.cand_key[i + u * kRowThreads] - base;
+      for (int u = 0; u < 4; ++u) off[u] = rs.cand_key[i + u * kRowThreads];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
-        if ((uint32_t)((uint64_t)off[u] >> top) == prefix) atomicAdd(&h[hslot((off[u] >> low) & dmask)], 1u);
+      for (int u = 0; u < 4; ++u) {
+        const uint32_t o = off[u] - base;
+        if (off[u] >= base && (uint32_t)((uint64_t)o >> top) == prefix) atomicAdd(&h[hslot((o >> low) & dmask)], 1u);
+      }
     }
     for (; i < n; i += kRowThreads) {
-      const uint32_t off = rs.cand_key[i] - base;
-      if ((uint32_t)((uint64_t)off >> top) == prefix) atomicAdd(&h[hslot((off >> low) & dmask)], 1u);
+      const uint32_t kk = rs.cand_key[i], o = kk - base;
+      if (kk >= base && (uint32_t)((uint64_t)o >> top) == prefix) atomicAdd(&h[hslot((o >> low) & dmask)], 1u);
     }
     __syncthreads();
     if ((tid >> 6) == 0) {
@@ -645,9 +656,7 @@ __device__ __forceinline__ int gather_segments(const uint32_t* __restrict__ ws, 
         if (v < n_spec) spec[w] = __builtin_amdgcn_raw_buffer_load_b128(pairs, (v * kSub + i) * 8, 0, 0);
       }
     }
-    uint32_t m = cut;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    const uint32_t m = wave_max(cut);
     // pairs not read ahead
     const uint32_t rest = (u < n_spec) ? (cnt > (uint32_t)kSpec ? cnt - kSpec : 0u) : cnt;
     uint32_t incl = cnt, rincl = rest, tot, rtot;
@@ -785,11 +794,11 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     clear_hist_row();  // wave 0 read it before the barrier
   }
   if (n >= k) {  // n < 0: more than kCap candidates
-    // a long row's candidates lie above high cuts, in a narrow key range
-    const Kth t = (!from_hist && len >= kRangedMinSegs * kSeg) ? select_candidates_ranged(n, k)
-                                                                : select_candidates(n, k, from_hist, bin0, above0);
+    // gathered candidates: the select over those at or above the largest cut
+    const Kth t = (!from_hist && len > kSeg) ? select_candidates_ranged(n, k, rs.max_cut)
+                                             : select_candidates(n, k, from_hist, bin0, above0);
     // every key a segment left out lies below its cut, hence below T
-    if (t.T >= rs.max_cut) {
+    if (t.r != 0xFFFFFFFFu && t.T >= rs.max_cut) {
       write_from_candidates(n, t, oi, ov, with_vals);
       return;
     }

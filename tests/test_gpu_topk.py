@@ -183,10 +183,11 @@ def test_too_few_candidates_falls_back(lib):
 
 
 def test_long_rows_with_narrow_candidate_ranges(lib):
-    """Rows of at least eight segments select over the candidates' own key
-    range: candidates that are all one value (no digit left to resolve),
-    two values one ulp apart, and ordinary random rows, with k around the
-    number of top values."""
+    """Rows longer than one segment select over the candidates at or above
+    the largest segment cut, on digits of their offset from it: candidates
+    that are all one value (no digit left to resolve), two values one ulp
+    apart, exactly k top values, a narrow range of all keys, and ordinary
+    random rows."""
     rng = np.random.default_rng(12)
     B, N, k = 6, 32768, 2048
     x = -np.abs(rng.standard_normal((B, N))).astype(np.float32) - 1.0  # everything below -1
