@@ -34,9 +34,9 @@
 // block with eight v_mfma_f32_32x32x16_bf16 (bf16 products, fp32
 // accumulation). The accumulator holds the 32 heads x 32 positions of each
 // half page with one position per lane; ReLU, the head weights and 16 of the
-// 32 heads are summed in registers, and one cross-half lane exchange adds the
-// other 16 heads. The tail is written with 16-byte stores, 1 KiB per wave
-// instruction.
+// 32 heads are summed in registers, and one cross-half lane exchange
+// (v_permlane32_swap) adds the other 16 heads. The tail is written with
+// 16-byte stores, 1 KiB per wave instruction.
 //
 // fp8 keys (score_kernel<true>): a page is 4 KiB of OCP FP8 E4M3 codes plus
 // one float32 scale per key. The codes are staged in LDS under an XOR swizzle
@@ -417,10 +417,12 @@ void score_kernel(
               p1 = __builtin_fmaf(wv[t][g][r], __builtin_fmaxf(acc1[4 * g + r], 0.f), p1);
             }
           }
-          p0 += __shfl_xor(p0, 32);
-          p1 += __shfl_xor(p1, 32);
-          // lane < 32 owns position lane of the first half, lane >= 32 position lane of the second
-          val[t] = half ? p1 : p0;
+          // lane < 32 owns position lane of the first half, lane >= 32 position lane of the second;
+          // the other 16 heads of a position sit in lane ^ 32: one v_permlane32_swap hands p0's upper
+          // half to the lower lanes and p1's lower half to the upper lanes
+          const auto sw = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, p0),
+                                                           __builtin_bit_cast(uint32_t, p1), false, false);
+          val[t] = half ? p1 + __builtin_bit_cast(float, (uint32_t)sw[0]) : p0 + __builtin_bit_cast(float, (uint32_t)sw[1]);
         }
       }
       if constexpr (kStashed) {
