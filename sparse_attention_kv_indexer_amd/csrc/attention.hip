@@ -93,7 +93,19 @@ __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
                                                  c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float xor_lanes(float v, int m) { return __shfl_xor(v, m, 64); }
+// Combine v over the four lanes l, l ^ 16, l ^ 32, l ^ 48 with op, in
+// registers: v_permlane32_swap of two copies of v leaves lane l's value and
+// lane l ^ 32's in the pair; v_permlane16_swap then does the same across
+// rows of 16 lanes.
+template <typename Op>
+__device__ __forceinline__ float xor_lanes_16_32(float v, Op op) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, v);
+  const auto a = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  const float w = op(__builtin_bit_cast(float, (uint32_t)a[0]), __builtin_bit_cast(float, (uint32_t)a[1]));
+  const uint32_t x = __builtin_bit_cast(uint32_t, w);
+  const auto b = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return op(__builtin_bit_cast(float, (uint32_t)b[0]), __builtin_bit_cast(float, (uint32_t)b[1]));
+}
 
 // Chunk c of staged row r sits at chunk c ^ (r & 7) of that row: the rows of
 // an aligned group of 8 put any given chunk in 8 different 16-byte slots of
@@ -273,8 +285,7 @@ void attention_kernel(const AttArgs a) {
       S[r] = ((mine >> r) & 1u) ? S[r] * a.c : -__builtin_inff();
       mt = fmaxf(mt, S[r]);
     }
-    mt = fmaxf(mt, xor_lanes(mt, 16));
-    mt = fmaxf(mt, xor_lanes(mt, 32));
+    mt = xor_lanes_16_32(mt, [](float x, float y) { return fmaxf(x, y); });
     *reinterpret_cast<f32x4*>(sbuf + (t & 1) * kSTile + s_wr) = S;
     if (g == 0) mbuf[t & 1][ph][16 * hh + j] = mt;
   };
@@ -373,8 +384,7 @@ void attention_kernel(const AttArgs a) {
   // Sums of weights of this lane's two heads over all lanes (g) of the wave.
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb) {
-    l_run[hb] += xor_lanes(l_run[hb], 16);
-    l_run[hb] += xor_lanes(l_run[hb], 32);
+    l_run[hb] = xor_lanes_16_32(l_run[hb], [](float x, float y) { return x + y; });
   }
   float* dst_o;
   float* dst_l;
