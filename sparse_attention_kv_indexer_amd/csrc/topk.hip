@@ -53,6 +53,11 @@ constexpr int kSegWaves = kSegThreads / 64;
 constexpr int kSeg = 4096;                    // positions per segment workgroup
 constexpr int kPerLane = kSeg / kSegThreads;  // 16 consecutive positions per lane
 constexpr int kSub = kSeg / kSegWaves;        // 1024 positions per wave: one sub-slot
+// Segment workgroups per request: each takes segments y, y + kSegGridY, ...
+// (rows of up to 32 segments, 128K tokens, get one workgroup per segment; a
+// wider row width no longer launches thousands of workgroups that only read a
+// short length and exit).
+constexpr int kSegGridY = 32;
 constexpr int kRecWords = 8;                  // per segment: kept count of each wave, cut key, unused
 
 constexpr int kRowThreads = 1024;             // row kernel
@@ -824,7 +829,7 @@ hipError_t launch_topk(const float* logits, const int32_t* seq_lens, int32_t bat
   uint32_t* ws = static_cast<uint32_t*>(workspace);
   // a row reaches the segment kernel only if it is longer than kSeg and than k
   if (max_c4 > kSeg && k < max_c4)
-    hipLaunchKernelGGL(topk_segment_kernel, dim3(batch, min(n_seg, 65535)), dim3(kSegThreads), 0, stream, logits, seq_lens,
+    hipLaunchKernelGGL(topk_segment_kernel, dim3(batch, min(n_seg, kSegGridY)), dim3(kSegThreads), 0, stream, logits, seq_lens,
                        max_c4, k, n_seg, ws, hist);
   hipLaunchKernelGGL(topk_row_kernel, dim3(batch), dim3(kRowThreads), 0, stream, logits, seq_lens, max_c4, k,
                      out_idx, out_vals, ws, n_seg, hist);
