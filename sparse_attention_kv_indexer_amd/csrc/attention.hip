@@ -181,21 +181,37 @@ void attention_kernel(const AttArgs a) {
   // Resolve every entry of the split to a pool row (page * 64 + slot row).
   const rsrc_t ir = make_rsrc(a.idx + (int64_t)b * a.k, (uint32_t)a.k * 4u);
   const rsrc_t pr = make_rsrc(a.page_table + (int64_t)b * a.max_pages, (uint32_t)a.max_pages * 4u);
+  // Every entry load of the lane first, then every page-table load: two
+  // memory round trips in all, whatever the number of entries per lane.
   const int width = a.max_pages * kPage;
+  constexpr int kPer = kMaxAttChunk / kAttThreads;  // entries per lane, at most
+  static_assert(kPer * kAttThreads == kMaxAttChunk, "entries per lane");
+  int pos[kPer], page[kPer];
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int u = tid + i * kAttThreads;
+    pos[i] = u < n ? (int)load_u32(ir, (g0 + u) * 4) : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const bool need = pos[i] >= 0 && pos[i] < width;
+    page[i] = need ? (int)load_u32(pr, (pos[i] >> 6) * 4) : 0;
+  }
   int bad = 0;
-  for (int u = tid; u < ntiles * kTile; u += kAttThreads) {
-    uint32_t v = kSkip;
-    if (u < n) {
-      const int pos = (int)load_u32(ir, (g0 + u) * 4);
-      if (pos >= width) {
+#pragma unroll
+  for (int i = 0; i < kPer; ++i) {
+    const int u = tid + i * kAttThreads;
+    if (u < ntiles * kTile) {
+      uint32_t v = kSkip;
+      if (pos[i] >= width) {
         v = kBad;
-      } else if (pos >= 0) {
-        const int page = (int)load_u32(pr, (pos >> 6) * 4);
-        v = (page < 0 || (int64_t)page >= a.num_pages) ? kBad : (uint32_t)page * kPage + (uint32_t)(pos & 63);
+      } else if (pos[i] >= 0) {
+        v = (page[i] < 0 || (int64_t)page[i] >= a.num_pages) ? kBad
+                                                            : (uint32_t)page[i] * kPage + (uint32_t)(pos[i] & 63);
       }
+      bad |= v == kBad;
+      rows[u] = v;
     }
-    bad |= v == kBad;
-    rows[u] = v;
   }
   bad = __syncthreads_or(bad);  // also publishes rows[]
 
