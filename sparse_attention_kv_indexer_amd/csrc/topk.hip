@@ -17,8 +17,9 @@
 // position order places every chosen position.
 //
 // Two kernels, so that no workgroup ever waits on another one:
-//  * Segment kernel (rows longer than kSeg positions only; grid: segments x
-//    requests, 256 lanes). A row is cut into segments of kSeg positions, so a
+//  * Segment kernel (rows longer than kSeg positions only; grid: requests x
+//    at most kSegGridY, 256 lanes, each workgroup taking every kSegGridY-th
+//    segment). A row is cut into segments of kSeg positions, so a
 //    long row is read by many compute units at once; lane t of a segment's
 //    workgroup holds the 16 consecutive positions at 16 t in registers. Two
 //    sampled keys per lane are counted into a histogram of the first digit,
@@ -31,12 +32,20 @@
 //    its own candidate set, read straight from the logits. A longer row
 //    gathers the sub-slots into LDS in order, hence position order: the first
 //    kSpec pairs of the first kSpecSlots sub-slots are loaded with 16-byte
-//    loads together with the counts, before the counts are known. An exact
-//    radix select over the candidates gives T; if T is at or above every
-//    segment's cut, each key a segment left out is below T, so the candidates
-//    hold the whole top k and the chosen positions are written from them.
-//    Otherwise (a cut above T, fewer than k or more than kCap candidates) the
-//    workgroup selects over the whole row instead, re-reading it from memory.
+//    loads together with the counts, before the counts are known. If T is
+//    at or above every segment's cut, each key a segment left out is below T,
+//    so the candidates hold the whole top k and the chosen positions are
+//    written from them; hence the exact radix select runs over the
+//    candidates at or above the largest cut only, on digits of their offset
+//    from it (a narrow key range, so the first pass spreads over many bins).
+//    Otherwise (fewer than k keys at or above the largest cut, or more than
+//    kCap candidates) the workgroup selects over the whole row instead,
+//    re-reading it from memory.
+//
+// With the score kernel's first-digit histogram of the row (the fused pair),
+// every segment cuts at the exact lower edge of the bin holding the k-th
+// largest key, the row kernel starts its select at the second digit, and it
+// sets the histogram back to zero.
 //
 // A radix pass counts into a histogram in LDS; one wave then reads the whole
 // histogram and finds the digit (in the segment kernel every wave does so
