@@ -293,10 +293,12 @@ def bench_attention(args, cfg, inp):
     alg = attention_bytes(inp, idx)
     achieved = alg["total"] / (call_ms * 1e-3) / 1e9
     nsplit = need // (B * wl.ATT_HEADS * (wl.ATT_VD + 1) * 4) if need else 1
+    att_traffic = read_traffic(cfg.name, ATT_TRAFFIC_FILE, ATT_SOURCES)
     roofline = {
         "bound": "hbm", "kernel": "attention_kernel + merge_kernel (one call)", "achieved": round(achieved, 1),
         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": read_traffic(cfg.name, ATT_TRAFFIC_FILE, ATT_SOURCES),
+        "traffic": (att_traffic or {}).get("total_bytes"),
+        "traffic_bytes": att_traffic,
         "algorithmic_bytes_per_launch": alg, "launch_avg_us": round(call_ms * 1e3, 3),
     }
     result = {
@@ -462,7 +464,8 @@ def main():
                            + (f"+tok{T}" if T > 1 else "") + ("+hist" if fused else ""))
     roofline = {
         "bound": "hbm", "kernel": "score_kernel", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+        "traffic": (traffic or {}).get("total_bytes"), "traffic_bytes": traffic,
         "algorithmic_bytes_per_launch": alg, "launch_avg_us": round(score_avg_ms * 1e3, 3),
         "k_bytes_only": {"achieved": round(k_only, 1), "frac": round(k_only / HBM_PEAK_GBS, 4)},
         "topk_launch_avg_us": round(topk_avg_ms * 1e3, 3),
