@@ -81,7 +81,8 @@ int dsa_indexer_last_hip_error(void);
  * request.
  *
  *   q          bf16  [batch][32][64], 16-byte aligned
- *   w          fp32  [batch][32]
+ *   w          fp32  [batch][32], 16-byte aligned (each request's 32 weights
+ *              are read as eight 16-byte vectors)
  *   k_pool     bf16  [num_pages][64][64], 16-byte aligned: page p, row i is the
  *              key of the position that maps to (p, i); dims contiguous
  *   num_pages  pages in k_pool (> 0)
@@ -125,7 +126,8 @@ int dsa_indexer_score(const void *q, const float *w, const void *k_pool, int64_t
  *              allocated; dsa_indexer_topk_hist sets it back to zero).
  *
  * Errors as for dsa_indexer_score (DSA_ERR_NULL also for a NULL hist,
- * DSA_ERR_ALIGN for a misaligned one).
+ * DSA_ERR_ALIGN for a misaligned one); q, w, k_pool and logits are 16-byte
+ * aligned as there.
  */
 int dsa_indexer_score_hist(const void *q, const float *w, const void *k_pool, int64_t num_pages,
                            const int32_t *page_table, const int32_t *seq_lens, int32_t batch,
@@ -146,7 +148,8 @@ int dsa_indexer_score_hist(const void *q, const float *w, const void *k_pool, in
  *              contiguous; 4 KiB per page
  *   k_scale    fp32  [num_pages][64], 4-byte aligned: the scale of each key
  *
- * Errors as for dsa_indexer_score (DSA_ERR_NULL also for a NULL k_scale).
+ * q, w and logits are 16-byte aligned as for dsa_indexer_score. Errors as for
+ * dsa_indexer_score (DSA_ERR_NULL also for a NULL k_scale).
  */
 int dsa_indexer_score_fp8(const void *q, const float *w, const void *k_pool_fp8, const float *k_scale,
                           int64_t num_pages, const int32_t *page_table, const int32_t *seq_lens,

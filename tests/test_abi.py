@@ -215,3 +215,24 @@ def test_score_mtp_shape(lib, over):
 @pytest.mark.parametrize("field,off", [("q", 8), ("w", 4), ("k_pool", 2), ("logits", 4), ("page_table", 2), ("seq_lens", 1)])
 def test_score_mtp_alignment(lib, field, off):
     assert lib.dsa_indexer_score_mtp(*mtp_args(**{field: A + off})) == ALIGN
+
+
+def _doc_of(name):
+    """The comment block right above a declaration in the header."""
+    text = open(HEADER).read()
+    at = text.index(f"int {name}(")
+    return text[text.rindex("/*", 0, at):at]
+
+
+@pytest.mark.parametrize("off", [4, 8, 12])
+def test_w_alignment_matches_the_header(lib, off):
+    """The header says w is 16-byte aligned for every score entry point, and a
+    w that is only 4-byte aligned is refused with DSA_ERR_ALIGN."""
+    assert re.search(r"\*\s+w\s+fp32\s+\[batch\]\[32\], 16-byte aligned", _doc_of("dsa_indexer_score"))
+    assert "q, w, k_pool and logits are 16-byte" in _doc_of("dsa_indexer_score_hist")
+    assert "q, w and logits are 16-byte aligned" in _doc_of("dsa_indexer_score_fp8")
+    assert re.search(r"\*\s+w\s+fp32\s+\[batch\]\[tokens\]\[32\], 16-byte aligned", _doc_of("dsa_indexer_score_mtp"))
+    assert lib.dsa_indexer_score(*score_args(w=A + off)) == ALIGN
+    assert lib.dsa_indexer_score_hist(*score_hist_args(w=A + off)) == ALIGN
+    assert lib.dsa_indexer_score_fp8(*score_fp8_args(w=A + off)) == ALIGN
+    assert lib.dsa_indexer_score_mtp(*mtp_args(w=A + off)) == ALIGN
