@@ -138,7 +138,8 @@ __device__ __forceinline__ void att_place(int nsplit, int& b, int& s) {
 // (lds is a wave-uniform LDS byte address). Issued as inline assembly so that the compiler does
 // not track it: its completion is awaited explicitly (s_waitcnt vmcnt, then a
 // barrier) before any wave reads the buffer. Extra outstanding loads can only
-// make the compiler's own vmcnt waits stricter, never looser.
+// make the compiler's own vmcnt waits stricter, never looser. m0 is listed as
+// clobbered, so the compiler keeps no value of its own there across the load.
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %1\n\t"
@@ -146,7 +147,7 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
       "global_load_lds_dwordx4 %0, off"
       :
       : "v"(src), "s"(lds)
-      : "memory");
+      : "memory", "m0");
 }
 
 // Encoding of s_waitcnt that waits until at most n vector-memory operations

@@ -289,18 +289,19 @@ void score_kernel(
     // never fall back to waiting for everything in flight.
     const rsrc_t none = make_rsrc(k_pool, 0u);
     const char* const kbase = static_cast<const char*>(k_pool);
-    // page id load of item x (pending until key_load reads it); 0 past the range
-    auto id_load = [&](uint32_t x, int& bx, uint32_t& jx) -> uint32_t {
-      const bool in = x < pe;
+    // page id load of item x (pending until key_load reads it); `in` tells
+    // whether x lies in the range (past it the load reads an empty resource)
+    auto id_load = [&](uint32_t x, int& bx, uint32_t& jx, bool& in) -> uint32_t {
+      in = x < pe;
       if (in) window_find(W, x, sh, false, bx, jx);
       const rsrc_t pt = in ? make_rsrc(page_table + (int64_t)bx * max_pages, (uint32_t)max_pages * 4u) : none;
       return __builtin_amdgcn_raw_buffer_load_b32(pt, in ? (int)jx * 4 : 0, 0, 0);
     };
-    // key page of a loaded id into dst; false if the id is outside the pool
-    // (then dst is zero and the page is never dereferenced)
-    auto key_load = [&](uint32_t id, Regs& dst) -> bool {
+    // key page of a loaded id into dst; false if the item is past the range
+    // or the id is outside the pool (then dst is zero and no page is read)
+    auto key_load = [&](uint32_t id, bool in, Regs& dst) -> bool {
       const int page = __builtin_amdgcn_readfirstlane((int)id);
-      const bool ok = page >= 0 && (int64_t)page < num_pages;
+      const bool ok = in && page >= 0 && (int64_t)page < num_pages;
       const rsrc_t kp = ok ? make_rsrc(kbase + (int64_t)page * Fmt::kBytes, Fmt::kBytes) : none;
       // 16-byte chunk c = 64 * i + lane of the page
 #pragma unroll
@@ -471,24 +472,24 @@ void score_kernel(
     Regs KA, KB;
     int bA = 0, bB = 0, bX = 0, bY = 0;
     uint32_t jA = 0, jB = 0, jX = 0, jY = 0, PX = 0, PY = 0;
-    bool okA = false, okB = false;
+    bool okA = false, okB = false, inA = false, inX = false, inY = false;
     uint32_t it = s;
-    const uint32_t PA = id_load(it, bA, jA);
-    PY = id_load(it + 1, bY, jY);
-    okA = key_load(PA, KA);
+    const uint32_t PA = id_load(it, bA, jA, inA);
+    PY = id_load(it + 1, bY, jY, inY);
+    okA = key_load(PA, inA, KA);
     for (;;) {
       // phase A: item it in KA; item it + 1's id in PY
       ensure_qw(bA);
-      PX = id_load(it + 2, bX, jX);
-      okB = key_load(PY, KB);
+      PX = id_load(it + 2, bX, jX, inX);
+      okB = key_load(PY, inY, KB);
       bB = bY;
       jB = jY;
       compute(bA, jA, okA, KA);
       if (++it >= pe) break;
       // phase B: item it in KB; item it + 1's id in PX
       ensure_qw(bB);
-      PY = id_load(it + 2, bY, jY);
-      okA = key_load(PX, KA);
+      PY = id_load(it + 2, bY, jY, inY);
+      okA = key_load(PX, inX, KA);
       bA = bX;
       jA = jX;
       compute(bB, jB, okB, KB);
