@@ -1,21 +1,28 @@
 """Decode-step benchmark of the DSA indexer on one MI355X.
 
 A step is the whole hot path over one batch: the score kernel (page walk,
-weighted-ReLU scores, -inf tail) followed by the top-k kernel, both replayed
+weighted-ReLU scores, -inf tail) followed by the top-k kernels, both replayed
 from a captured HIP graph. Inputs are seeded synthetic tensors already
 resident in HBM; R identical copies at different addresses are used round
 robin so that every step reads its keys from HBM, not from the 256 MB
 Infinity Cache.
 
 Prints one JSON line. ``value`` is valid positions scored per second over the
-timed steps; ``roofline`` prices the score kernel's algorithmic bytes per
-launch against the 8 TB/s HBM peak, using its average launch duration
-measured here with HIP events; ``cpu_baseline`` times the float64 CPU oracle
-on the host cores over a bounded sample of the same workload.
+timed steps of the headline workload (B=64, 128K-token context, uniform
+lengths). ``roofline`` prices the score kernel's valid-page key bytes per
+launch against the 8 TB/s HBM peak, with its average launch duration measured
+here with HIP events (median of five batches), and against two ceilings
+measured in the same run by the HBM read probes (one long contiguous read,
+and random 8 KiB pages read like the score kernel reads its keys).
+``workloads`` holds the same figures for the all-pages-valid workload and
+for the 1M-token and 8K-token row widths at 512-token lengths in both tail
+modes, with the stress ratio between them. ``cpu_baseline`` times the float64
+CPU oracle, requests spread over the host's cores, on the same workload.
 """
 from __future__ import annotations
 
 import argparse
+import ctypes
 import hashlib
 import json
 import math
@@ -31,6 +38,7 @@ MALL_BYTES = 256 << 20  # Infinity Cache
 METRIC = "valid positions scored/s + µs/step at B=64,128K ctx; % of HBM roofline"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.txt")
 SCORE_SOURCES = ["sparse_attention_kv_indexer_amd/csrc/score.hip", "sparse_attention_kv_indexer_amd/csrc/common.h"]
+BATCHES = 5  # timed batches; the launch averages are their median
 
 
 def parse():
@@ -52,7 +60,11 @@ def parse():
                     help="hist: the score kernel counts each row's first-digit histogram and the top-k starts "
                          "from it (score_hist + topk_hist); sampled: the top-k samples its own cut")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-reps", type=int, default=3)
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only --config (no extra workloads, no stress ratio, no probes)")
+    ap.add_argument("--probe", action="store_true",
+                    help="only run the HBM read probes and print their JSON line")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0, help="wall-clock budget of the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain device-to-device copy of known size (reference for HBM byte counters)")
     return ap.parse_args()
@@ -123,52 +135,424 @@ def algorithmic_bytes(inp, hwm: bool, tokens: int = 1, token_lens=None) -> dict:
             "total": k_bytes + out_bytes + table_bytes + req_bytes}
 
 
-def cpu_baseline(inp, reps: int, total_s: float = 12.0) -> dict:
-    """The oracle, as it stands, on the host: score + top-k of the whole step
-    (or of its first requests when one step alone exceeds the per-repetition
-    budget), repeated at least `reps` times and until about total_s seconds
-    of CPU work are done; the median repetition is reported."""
+# ---------------------------------------------------------------------------
+# CPU baseline: the oracle, as it stands, with requests spread over processes
+# ---------------------------------------------------------------------------
+
+_CPU_INP = None  # the workload, inherited by the forked workers
+
+
+def _cpu_worker_init():
+    try:
+        from threadpoolctl import threadpool_limits
+
+        threadpool_limits(1)  # one BLAS thread per worker process
+    except Exception:
+        pass
+
+
+def _cpu_rows(rows):
+    """Score + top-k of requests `rows` by the oracle (in a worker)."""
     import numpy as np
 
     import oracle
 
-    try:
-        from threadpoolctl import threadpool_info
+    inp = _CPU_INP
+    r = np.asarray(rows)
+    if inp.fp8:
+        s = oracle.score_fp8(inp.q_bits[r], inp.w[r], inp.k8, inp.k_scale, inp.page_table[r], inp.seq_lens[r])
+    else:
+        s = oracle.score(inp.q_bits[r], inp.w[r], inp.k_bits, inp.page_table[r], inp.seq_lens[r])
+    oracle.topk(s, inp.seq_lens[r], inp.topk)
+    return len(rows)
 
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # threadpoolctl missing: numpy's BLAS default is one thread per core
-        threads = os.cpu_count() or 1
-    rows = inp.batch
-    budget_s = 10.0
+
+def cpu_baseline(inp, seconds: float) -> dict:
+    """The float64 oracle, unchanged, on the host: the step's requests are
+    spread over one worker process per core the process may run on (each with
+    one BLAS thread), and whole steps are repeated for about `seconds` of
+    wall-clock time; the median step is reported. Called before the GPU is
+    touched, so the workers are forked from a process without a GPU context."""
+    import multiprocessing as mp
+
+    import numpy as np
+
+    global _CPU_INP
+    _CPU_INP = inp
+    cores = len(os.sched_getaffinity(0))
+    workers = max(1, min(cores, inp.batch))
+    # longest requests first, dealt round robin, so the workers' shares are even
+    order = np.argsort(-np.clip(inp.seq_lens, 0, inp.max_c4), kind="stable")
+    chunks = [order[i::workers].tolist() for i in range(workers)]
+    ctx = mp.get_context("fork")
     times = []
-    spent = 0.0
-    while len(times) < max(reps, 1) or (spent < total_s and len(times) < 200):
-        sub = inp
-        if rows < inp.batch:
-            sub = type(inp)(inp.q_bits[:rows], inp.w[:rows], inp.k_bits, inp.page_table[:rows],
-                            inp.seq_lens[:rows], inp.topk, inp.k8, inp.k_scale)
-        t0 = time.perf_counter()
-        if sub.fp8:
-            s = oracle.score_fp8(sub.q_bits, sub.w, sub.k8, sub.k_scale, sub.page_table, sub.seq_lens)
-        else:
-            s = oracle.score(sub.q_bits, sub.w, sub.k_bits, sub.page_table, sub.seq_lens)
-        oracle.topk(s, sub.seq_lens, sub.topk)
-        dt = time.perf_counter() - t0
-        spent += dt
-        times.append(dt)
-        if dt > budget_s and rows > 1:  # shrink the sample for the remaining repetitions
-            rows = max(1, int(rows * budget_s / dt))
-            times = []
+    with ctx.Pool(workers, initializer=_cpu_worker_init) as pool:
+        pool.map(_cpu_rows, [[c[0]] for c in chunks if c])  # warm the workers up
+        t_end = time.perf_counter() + seconds
+        while len(times) < 3 or (time.perf_counter() < t_end and len(times) < 200):
+            t0 = time.perf_counter()
+            pool.map(_cpu_rows, chunks, chunksize=1)
+            times.append(time.perf_counter() - t0)
+    _CPU_INP = None
     dt = sorted(times)[len(times) // 2]
-    valid = int(np.clip(inp.seq_lens[:rows], 0, inp.max_c4).sum())
+    valid = int(np.clip(inp.seq_lens, 0, inp.max_c4).sum())
     try:
         cpu = [l.split(":", 1)[1].strip() for l in open("/proc/cpuinfo") if l.startswith("model name")][0]
     except Exception:
         cpu = "unknown"
-    return {"value": valid / dt, "unit": "valid positions/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"score + top-{inp.topk} of {rows} of {inp.batch} requests ({valid} valid positions), "
-                      f"float64 numpy oracle, median of {len(times)} repetitions ({spent:.1f} s in all), "
-                      f"{dt:.3f} s each; cpu {cpu}"}
+    return {"value": valid / dt, "unit": "valid positions/s", "cores": workers, "kind": "oracle",
+            "sample": f"score + top-{inp.topk} of all {inp.batch} requests ({valid} valid positions) per step, "
+                      f"float64 numpy oracle, requests spread over {workers} worker processes (one BLAS thread "
+                      f"each; {cores} cores available), median of {len(times)} steps, {dt:.3f} s each; cpu {cpu}"}
+
+
+# ---------------------------------------------------------------------------
+# HBM read probes
+# ---------------------------------------------------------------------------
+
+def _median(xs):
+    xs = sorted(xs)
+    return xs[len(xs) // 2]
+
+
+def timed_batches(launch, n: int, batches: int = BATCHES):
+    """Median per-launch ms over `batches` batches of n launches each, queued
+    back to back behind a spin kernel (so the host never starves the GPU) and
+    bracketed by HIP events on the launching stream."""
+    import torch
+
+    out = []
+    for _ in range(batches):
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda._sleep(int(2.4e9 * 0.01))  # ~10 ms of queued work ahead of the launches
+        s.record()
+        for i in range(n):
+            launch(i)
+        e.record()
+        torch.cuda.synchronize()
+        out.append(s.elapsed_time(e) / n)
+    return _median(out)
+
+
+def probes(page_counts, cu_count: int) -> dict:
+    """Achievable HBM read rates on this GPU: a 1 GiB contiguous read, and
+    random 8 KiB pages from a 512 MiB pool for each page count (the valid
+    pages of a workload), on the score kernel's grid of one-wave workgroups."""
+    import numpy as np
+    import torch
+
+    from sparse_attention_kv_indexer_amd import build
+
+    lib = ctypes.CDLL(build.PROBE_LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.dsa_probe_stream_read.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_int, vp]
+    lib.dsa_probe_page_read.argtypes = [vp, ctypes.c_uint64, vp, ctypes.c_int, vp, ctypes.c_int, vp]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    res = {}
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    grid_s = cu_count * 8
+    out = torch.empty(grid_s * 256, dtype=torch.int32, device="cuda")
+
+    def stream_launch(_):
+        rc = lib.dsa_probe_stream_read(src.data_ptr(), nbytes, out.data_ptr(), grid_s, st)
+        assert rc == 0, rc
+
+    for _ in range(3):
+        stream_launch(0)
+    ms = timed_batches(stream_launch, 10)
+    res["stream_read"] = {"bytes": nbytes, "us": round(ms * 1e3, 2), "GBs": round(nbytes / (ms * 1e-3) / 1e9, 1)}
+    del src
+    pool_pages = 65536  # 512 MiB of 8 KiB pages: twice the Infinity Cache
+    pool = torch.empty(pool_pages * 8192, dtype=torch.uint8, device="cuda").fill_(3)
+    grid_p = cu_count * 12  # the score kernel's grid
+    outp = torch.empty(grid_p * 64, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(0)
+    for name, n in page_counts.items():
+        ids_np = rng.permutation(pool_pages)[:n].astype(np.int32)
+        assert 0 < n <= pool_pages and ids_np.min() >= 0 and ids_np.max() < pool_pages
+        ids = torch.from_numpy(ids_np).cuda()
+
+        def page_launch(_):
+            rc = lib.dsa_probe_page_read(pool.data_ptr(), pool_pages * 8192, ids.data_ptr(), n, outp.data_ptr(),
+                                         grid_p, st)
+            assert rc == 0, rc
+
+        for _ in range(3):
+            page_launch(0)
+        ms = timed_batches(page_launch, 20)
+        res[f"page_read_{name}"] = {"pages": n, "bytes": n * 8192, "us": round(ms * 1e3, 2),
+                                    "GBs": round(n * 8192 / (ms * 1e-3) / 1e9, 1)}
+    torch.cuda.synchronize()
+    return res
+
+
+# ---------------------------------------------------------------------------
+# The indexer step
+# ---------------------------------------------------------------------------
+
+def cu_count() -> int:
+    import torch
+
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def measure_step(cfg_name: str, steps: int, warmup: int, hwm=False, keys="bf16", T=1, fused=False, rotate=0,
+                 inp=None) -> dict:
+    """One workload: R input copies, one captured graph of [score; top-k]
+    per copy, `warmup` untimed replays, then exactly `steps` timed replays in
+    BATCHES batches (events between batches, no synchronization), and the
+    median per-launch duration of the score and top-k calls alone."""
+    import numpy as np
+    import torch
+
+    from sparse_attention_kv_indexer_amd import binding, workloads as wl
+
+    cfg = wl.CONFIGS[cfg_name]
+    if inp is None:
+        inp = wl.generate(cfg)
+    if keys == "fp8":
+        inp = wl.to_fp8(inp)
+    dev = torch.device("cuda:0")
+    base = binding.to_device(inp, dev)
+    mt = None
+    if T > 1:
+        mt = wl.mtp_inputs(inp, T, cfg.seed)
+        base["q"] = torch.from_numpy(mt.q_bits.view("int16")).to(dev).view(torch.bfloat16)
+        base["w"] = torch.from_numpy(mt.w).to(dev)
+        base["seq_lens"] = torch.from_numpy(mt.seq_lens).to(dev)
+    B, N, k = inp.batch, inp.max_c4, inp.topk
+    set_bytes = (inp.k8.nbytes + inp.k_scale.nbytes if inp.fp8 else inp.k_bits.nbytes) + T * B * N * 4
+    R = rotate or min(16, max(2, math.ceil(2 * MALL_BYTES / set_bytes)))
+    sets = []
+    for r in range(R):
+        t = {name: (v if r == 0 else v.clone()) for name, v in base.items()}
+        t["logits"] = torch.full((B * T, N), float("-inf"), dtype=torch.float32, device=dev)
+        t["hwm"] = torch.zeros(B, dtype=torch.int32, device=dev) if hwm else None
+        t["idx"] = torch.empty((B * T, k), dtype=torch.int32, device=dev)
+        t["vals"] = torch.empty((B * T, k), dtype=torch.float32, device=dev)
+        t["hist"] = binding.hist_buffer(B, dev) if fused else None
+        sets.append(t)
+
+    def launch_score(t):
+        if T > 1:
+            binding.score_mtp(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"],
+                              out=t["logits"].view(B, T, N))
+        elif inp.fp8:
+            binding.score_fp8(t["q"], t["w"], t["k8"], t["k_scale"], t["page_table"], t["seq_lens"], out=t["logits"],
+                              row_hwm=t["hwm"])
+        elif fused:
+            binding.score_hist(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"], t["hist"],
+                               out=t["logits"], row_hwm=t["hwm"])
+        else:
+            binding.score(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"], out=t["logits"],
+                          row_hwm=t["hwm"])
+
+    def launch_topk(t):
+        binding.topk(t["logits"], t["seq_lens"].view(-1), k, out_idx=t["idx"], out_vals=t["vals"], hist=t["hist"])
+
+    def launch_step(t):
+        launch_score(t)
+        launch_topk(t)
+
+    # warm up eagerly once per set (also brings row_hwm to its steady state)
+    for t in sets:
+        launch_step(t)
+    torch.cuda.synchronize()
+
+    # one captured graph per input copy: [score; top-k]
+    graphs = []
+    cap = torch.cuda.Stream()
+    cap.wait_stream(torch.cuda.current_stream())
+    for t in sets:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            launch_step(t)
+        graphs.append(g)
+    torch.cuda.synchronize()
+
+    for i in range(warmup):
+        graphs[i % R].replay()
+    torch.cuda.synchronize()
+    # exactly `steps` replays between one synchronized start and end, with
+    # events at the batch boundaries only
+    cuts = [round(steps * j / BATCHES) for j in range(BATCHES + 1)]
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(BATCHES + 1)]
+    evs[0].record()
+    i = 0
+    for j in range(BATCHES):
+        while i < cuts[j + 1]:
+            graphs[i % R].replay()
+            i += 1
+        evs[j + 1].record()
+    torch.cuda.synchronize()
+    total_ms = evs[0].elapsed_time(evs[-1])
+    batch_ms = [evs[j].elapsed_time(evs[j + 1]) / (cuts[j + 1] - cuts[j]) for j in range(BATCHES) if cuts[j + 1] > cuts[j]]
+
+    n_kern = 200
+    if fused:
+        # the top-k consumes (and zeroes) the histogram its score call filled,
+        # so it is timed as whole steps minus the score kernel alone; the
+        # score kernel's own back-to-back launches leave the histograms dirty,
+        # so they go last
+        step_avg_ms = timed_batches(lambda i: launch_step(sets[i % R]), n_kern)
+        score_avg_ms = timed_batches(lambda i: launch_score(sets[i % R]), n_kern)
+        topk_avg_ms = step_avg_ms - score_avg_ms
+    else:
+        score_avg_ms = timed_batches(lambda i: launch_score(sets[i % R]), n_kern)
+        topk_avg_ms = timed_batches(lambda i: launch_topk(sets[i % R]), n_kern)
+
+    valid = int(np.clip(inp.seq_lens if mt is None else mt.seq_lens, 0, N).sum())
+    alg = algorithmic_bytes(inp, hwm, T, None if mt is None else mt.seq_lens)
+    res = {
+        "inp": inp, "cfg": cfg, "R": R, "valid": valid, "T": T, "alg": alg,
+        "ms_per_step": total_ms / steps, "step_us_median_of_batches": _median(batch_ms) * 1e3,
+        "score_us": score_avg_ms * 1e3, "topk_us": topk_avg_ms * 1e3,
+        "k_GBs": alg["k"] / (score_avg_ms * 1e-3) / 1e9,
+        "all_GBs": alg["total"] / (score_avg_ms * 1e-3) / 1e9,
+    }
+    del sets, graphs, base
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def summary(r: dict) -> dict:
+    """The per-workload figures carried in the JSON line."""
+    return {
+        "workload": f"{r['cfg'].name}: {r['cfg'].description}",
+        "us_per_step": round(r["ms_per_step"] * 1e3, 2),
+        "step_us_median_of_batches": round(r["step_us_median_of_batches"], 2),
+        "valid_positions": r["valid"],
+        "valid_positions_per_s": r["valid"] / (r["ms_per_step"] * 1e-3),
+        "score_us": round(r["score_us"], 2), "topk_us": round(r["topk_us"], 2),
+        "score_key_GBs": round(r["k_GBs"], 1), "score_key_frac": round(r["k_GBs"] / HBM_PEAK_GBS, 4),
+        "score_all_bytes_frac": round(r["all_GBs"] / HBM_PEAK_GBS, 4),
+        "input_copies": r["R"],
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU only (no cross-GPU sharding or collectives); "
+              "run it with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+
+    from sparse_attention_kv_indexer_amd import workloads as wl
+
+    cfg = wl.CONFIGS[args.config]
+    T = args.tokens
+    if args.stage == "indexer" and not args.probe and not args.copy_calibration:
+        if T != 1 and (args.keys == "fp8" or args.hwm or not 1 <= T <= 4):
+            print("bench.py: --tokens 2..4 runs bf16 keys with the stateless tail", file=sys.stderr)
+            sys.exit(2)
+        if args.topk == "hist" and (T != 1 or args.keys == "fp8"):
+            print("bench.py: --topk hist runs one query token with bf16 keys", file=sys.stderr)
+            sys.exit(2)
+    inp = wl.generate(cfg) if not (args.probe or args.copy_calibration) else None
+
+    # the CPU baseline runs first, so its worker processes fork from a process
+    # that has not touched the GPU
+    cpu = None
+    if args.stage == "indexer" and inp is not None and not args.no_cpu and T == 1:
+        cpu = cpu_baseline(wl.to_fp8(inp) if args.keys == "fp8" else inp, args.cpu_seconds)
+
+    import torch
+
+    from sparse_attention_kv_indexer_amd import binding
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    binding.load()
+    if args.probe:
+        print(json.dumps({"probe": probes({"c3": 17511, "full": 32768}, cu_count())}), flush=True)
+        return
+    if args.stage == "attention":
+        bench_attention(args, cfg, inp)
+        return
+
+    fused = args.topk == "hist"
+    head = measure_step(args.config, args.steps, args.warmup, hwm=args.hwm, keys=args.keys, T=T, fused=fused,
+                        rotate=args.rotate, inp=inp)
+    inp = head["inp"]
+    alg = head["alg"]
+    traffic = read_traffic(args.config + ("+hwm" if args.hwm else "") + ("+fp8" if inp.fp8 else "")
+                           + (f"+tok{T}" if T > 1 else "") + ("+hist" if fused else ""))
+    roofline = {
+        "bound": "hbm", "kernel": "score_kernel", "numerator": "valid-page key bytes per launch",
+        "achieved": round(head["k_GBs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(head["k_GBs"] / HBM_PEAK_GBS, 4),
+        "traffic": (traffic or {}).get("total_bytes"), "traffic_bytes": traffic,
+        "algorithmic_bytes_per_launch": alg, "launch_avg_us": round(head["score_us"], 3),
+        "launch_avg": f"median of {BATCHES} batches of 200 back-to-back launches, HIP events",
+        "all_bytes": {"achieved": round(head["all_GBs"], 1), "frac": round(head["all_GBs"] / HBM_PEAK_GBS, 4)},
+        "topk_launch_avg_us": round(head["topk_us"], 3),
+        "topk_path": "score_hist + topk_hist (histogram from the score kernel)" if fused else "sampled cut",
+    }
+    result = {
+        "metric": METRIC,
+        "value": head["valid"] / (head["ms_per_step"] * 1e-3),
+        "unit": "valid positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": head["ms_per_step"],
+        "us_per_step": head["ms_per_step"] * 1e3,
+        "step_us_median_of_batches": round(head["step_us_median_of_batches"], 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{cfg.name}: {cfg.description}",
+            "batch": inp.batch, "heads": wl.HEADS, "dim": wl.DIM, "page_positions": wl.PAGE,
+            "max_pages": inp.max_pages, "max_c4": inp.max_c4, "valid_positions": head["valid"],
+            "valid_pages": int(wl.pages_needed(inp.seq_lens).sum()), "topk": inp.topk, "seed": cfg.seed,
+            "tail": "incremental (row_hwm)" if args.hwm else "stateless full -inf",
+            "input_copies": head["R"], "timing": f"hipGraph replay of [score; top-k], HIP events, {BATCHES} batches",
+            "accumulate": "fp32",
+            "keys": "e4m3fn codes + float32 scale per key" if inp.fp8 else "bf16",
+            "query_tokens": T,
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    if T > 1:
+        result["metric"] = METRIC + f" ({T} query tokens per request: token-positions scored/s)"
+        result["unit"] = "valid token-positions/s"
+    del head, inp
+    if not args.no_extra:
+        xs = min(args.steps, 200) if args.steps >= 20 else 20
+        xw = max(args.warmup, 5)
+        full = measure_step("full", xs, xw)
+        extra = {"full": summary(full)}
+        for name in ("stress8k", "stress1m"):
+            for hwm in (False, True):
+                r = measure_step(name, xs, xw, hwm=hwm)
+                extra[name + ("+hwm" if hwm else "")] = summary(r)
+        step = {key: extra[key]["us_per_step"] for key in extra}
+        result["workloads"] = extra
+        result["stress_ratio"] = {
+            "definition": "step time of stress1m / step time of stress8k (1M- vs 8K-token row width, "
+                          "every length 512 tokens); target <= 1.2",
+            "incremental_tail": round(step["stress1m+hwm"] / step["stress8k+hwm"], 3),
+            "incremental_vs_stateless_8k": round(step["stress1m+hwm"] / step["stress8k"], 3),
+            "stateless": round(step["stress1m"] / step["stress8k"], 3),
+        }
+        pr = probes({"c3": result["config"]["valid_pages"], "full": full["inp"].batch * full["inp"].max_pages},
+                    cu_count())
+        roofline["measured_ceiling"] = pr
+        roofline["frac_of_page_read"] = round(roofline["achieved"] / pr["page_read_c3"]["GBs"], 4)
+        roofline["frac_of_stream_read"] = round(roofline["achieved"] / pr["stream_read"]["GBs"], 4)
+        extra["full"]["score_key_frac_of_page_read"] = round(full["k_GBs"] / pr["page_read_full"]["GBs"], 4)
+    print(json.dumps(result), flush=True)
 
 
 ATT_METRIC = "selected positions attended/s + µs/step (sparse attention after the indexer); % of HBM roofline"
@@ -193,12 +577,11 @@ def attention_bytes(inp, idx) -> dict:
             "total": lat + sel + pages * 4 + q + out}
 
 
-def attention_cpu_baseline(inp, att, idx, reps: int, total_s: float = 12.0) -> dict:
+def attention_cpu_baseline(inp, att, idx, total_s: float = 12.0) -> dict:
     """The attention oracle on the host over the first requests of the step
-    (as many as fit about 2 s per repetition), repeated at least `reps` times
-    and until about total_s seconds; the median repetition is reported."""
-    import numpy as np
-
+    (as many as fit about 2 s per repetition), repeated at least 3 times and
+    until about total_s seconds; the median repetition is reported. numpy's
+    BLAS runs each product on its own threads."""
     import oracle
     from sparse_attention_kv_indexer_amd import workloads as wl
 
@@ -209,7 +592,7 @@ def attention_cpu_baseline(inp, att, idx, reps: int, total_s: float = 12.0) -> d
     except Exception:
         threads = os.cpu_count() or 1
     rows, times, spent = inp.batch, [], 0.0
-    while len(times) < max(reps, 1) or (spent < total_s and len(times) < 200):
+    while len(times) < 3 or (spent < total_s and len(times) < 200):
         t0 = time.perf_counter()
         oracle.sparse_attention(att.q_bits[:rows], att.kv_bits, inp.page_table[:rows], idx[:rows], att.scale,
                                 wl.ATT_VD)
@@ -223,8 +606,8 @@ def attention_cpu_baseline(inp, att, idx, reps: int, total_s: float = 12.0) -> d
     n = int((idx[:rows] >= 0).sum())
     return {"value": n / dt, "unit": "selected positions/s", "cores": int(threads), "kind": "oracle",
             "sample": f"attention of {rows} of {inp.batch} requests ({n} selected positions), float64 numpy "
-                      f"oracle, median of {len(times)} repetitions ({spent:.1f} s in all), {dt:.3f} s each"}
-
+                      f"oracle (BLAS threads: {threads}), median of {len(times)} repetitions ({spent:.1f} s in all), "
+                      f"{dt:.3f} s each"}
 
 def bench_attention(args, cfg, inp):
     """Sparse attention of 32 heads over a top-k-shaped selection (k entries,
@@ -320,190 +703,10 @@ def bench_attention(args, cfg, inp):
         "cpu_baseline": None,
     }
     if not args.no_cpu:
-        result["cpu_baseline"] = attention_cpu_baseline(inp, att, idx, args.cpu_reps)
+        result["cpu_baseline"] = attention_cpu_baseline(inp, att, idx)
     print(json.dumps(result), flush=True)
 
 
-def main():
-    args = parse()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this path runs on one GPU only (no cross-GPU sharding or collectives); "
-              "run it with --gpus 1", file=sys.stderr)
-        sys.exit(2)
-
-    import numpy as np
-    import torch
-
-    from sparse_attention_kv_indexer_amd import binding, workloads as wl
-
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    if args.copy_calibration:
-        copy_calibration()
-        return
-    binding.load()
-    cfg = wl.CONFIGS[args.config]
-    inp = wl.generate(cfg)
-    if args.stage == "attention":
-        torch.cuda.set_device(0)
-        bench_attention(args, cfg, inp)
-        return
-    T = args.tokens
-    if T != 1 and (args.keys == "fp8" or args.hwm or not 1 <= T <= 4):
-        print("bench.py: --tokens 2..4 runs bf16 keys with the stateless tail", file=sys.stderr)
-        sys.exit(2)
-    fused = args.topk == "hist"
-    if fused and (T != 1 or args.keys == "fp8"):
-        print("bench.py: --topk hist runs one query token with bf16 keys", file=sys.stderr)
-        sys.exit(2)
-    if args.keys == "fp8":
-        inp = wl.to_fp8(inp)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-
-    base = binding.to_device(inp, dev)
-    mt = None
-    if T > 1:
-        mt = wl.mtp_inputs(inp, T, cfg.seed)
-        base["q"] = torch.from_numpy(mt.q_bits.view("int16")).to(dev).view(torch.bfloat16)
-        base["w"] = torch.from_numpy(mt.w).to(dev)
-        base["seq_lens"] = torch.from_numpy(mt.seq_lens).to(dev)
-    B, N, k = inp.batch, inp.max_c4, inp.topk
-    set_bytes = (inp.k8.nbytes + inp.k_scale.nbytes if inp.fp8 else inp.k_bits.nbytes) + T * B * N * 4
-    R = args.rotate or min(16, max(2, math.ceil(2 * MALL_BYTES / set_bytes)))
-    sets = []
-    for r in range(R):
-        t = {name: (v if r == 0 else v.clone()) for name, v in base.items()}
-        t["logits"] = torch.full((B * T, N), float("-inf"), dtype=torch.float32, device=dev)
-        t["hwm"] = torch.zeros(B, dtype=torch.int32, device=dev) if args.hwm else None
-        t["idx"] = torch.empty((B * T, k), dtype=torch.int32, device=dev)
-        t["vals"] = torch.empty((B * T, k), dtype=torch.float32, device=dev)
-        t["hist"] = binding.hist_buffer(B, dev) if fused else None
-        sets.append(t)
-
-    def launch_score(t):
-        if T > 1:
-            binding.score_mtp(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"],
-                              out=t["logits"].view(B, T, N))
-        elif inp.fp8:
-            binding.score_fp8(t["q"], t["w"], t["k8"], t["k_scale"], t["page_table"], t["seq_lens"], out=t["logits"],
-                              row_hwm=t["hwm"])
-        elif fused:
-            binding.score_hist(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"], t["hist"],
-                               out=t["logits"], row_hwm=t["hwm"])
-        else:
-            binding.score(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"], out=t["logits"],
-                          row_hwm=t["hwm"])
-
-    def launch_topk(t):
-        binding.topk(t["logits"], t["seq_lens"].view(-1), k, out_idx=t["idx"], out_vals=t["vals"], hist=t["hist"])
-
-    def launch_step(t):
-        launch_score(t)
-        launch_topk(t)
-
-    # warm up eagerly once per set (also brings row_hwm to its steady state)
-    for t in sets:
-        launch_score(t)
-        launch_topk(t)
-    torch.cuda.synchronize()
-
-    # one captured graph per input copy: [score; top-k]
-    graphs = []
-    cap = torch.cuda.Stream()
-    cap.wait_stream(torch.cuda.current_stream())
-    for t in sets:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g, stream=cap):
-            launch_score(t)
-            launch_topk(t)
-        graphs.append(g)
-    torch.cuda.synchronize()
-
-    for i in range(args.warmup):
-        graphs[i % R].replay()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for i in range(args.steps):
-        graphs[i % R].replay()
-    end.record()
-    torch.cuda.synchronize()
-    ms_per_step = start.elapsed_time(end) / args.steps
-
-    # average launch duration of each kernel: n launches queued back to back on
-    # the launching stream behind a spin kernel (so the host never starves the
-    # GPU), bracketed by one pair of HIP events
-    def per_launch_ms(fn, n):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        torch.cuda._sleep(int(2.4e9 * 0.02))  # ~20 ms of queued work ahead of the launches
-        s.record()
-        for i in range(n):
-            fn(sets[i % R])
-        e.record()
-        torch.cuda.synchronize()
-        return s.elapsed_time(e) / n
-
-    n_kern = max(10, min(args.steps, 200))
-    if fused:
-        # the top-k consumes (and zeroes) the histogram its score call filled, so
-        # it is timed as whole steps minus the score kernel alone; the score
-        # kernel's own back-to-back launches leave the histograms dirty, so
-        # they go last
-        step_avg_ms = per_launch_ms(launch_step, n_kern)
-        score_avg_ms = per_launch_ms(launch_score, n_kern)
-        topk_avg_ms = step_avg_ms - score_avg_ms
-    else:
-        score_avg_ms = per_launch_ms(launch_score, n_kern)
-        topk_avg_ms = per_launch_ms(launch_topk, n_kern)
-
-    valid = int(np.clip(inp.seq_lens if mt is None else mt.seq_lens, 0, N).sum())
-    alg = algorithmic_bytes(inp, args.hwm, T, None if mt is None else mt.seq_lens)
-    achieved = alg["total"] / (score_avg_ms * 1e-3) / 1e9
-    k_only = alg["k"] / (score_avg_ms * 1e-3) / 1e9
-    traffic = read_traffic(args.config + ("+hwm" if args.hwm else "") + ("+fp8" if inp.fp8 else "")
-                           + (f"+tok{T}" if T > 1 else "") + ("+hist" if fused else ""))
-    roofline = {
-        "bound": "hbm", "kernel": "score_kernel", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-        "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-        "traffic": (traffic or {}).get("total_bytes"), "traffic_bytes": traffic,
-        "algorithmic_bytes_per_launch": alg, "launch_avg_us": round(score_avg_ms * 1e3, 3),
-        "k_bytes_only": {"achieved": round(k_only, 1), "frac": round(k_only / HBM_PEAK_GBS, 4)},
-        "topk_launch_avg_us": round(topk_avg_ms * 1e3, 3),
-        "topk_path": "score_hist + topk_hist (histogram from the score kernel)" if fused else "sampled cut",
-    }
-    result = {
-        "metric": METRIC,
-        "value": valid / (ms_per_step * 1e-3),
-        "unit": "valid positions/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_per_step,
-        "us_per_step": ms_per_step * 1e3,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {
-            "workload": f"{cfg.name}: {cfg.description}",
-            "batch": B, "heads": wl.HEADS, "dim": wl.DIM, "page_positions": wl.PAGE, "max_pages": inp.max_pages,
-            "max_c4": N, "valid_positions": valid, "valid_pages": int(wl.pages_needed(inp.seq_lens).sum()),
-            "topk": k, "seed": cfg.seed, "tail": "incremental (row_hwm)" if args.hwm else "stateless full -inf",
-            "input_copies": R, "timing": "hipGraph replay of [score; top-k], HIP events",
-            "accumulate": "fp32",
-            "keys": "e4m3fn codes + float32 scale per key" if inp.fp8 else "bf16",
-            "query_tokens": T,
-        },
-        "roofline": roofline,
-        "cpu_baseline": None,
-    }
-    if T > 1:
-        result["metric"] = METRIC + f" ({T} query tokens per request: token-positions scored/s)"
-        result["unit"] = "valid token-positions/s"
-    if not args.no_cpu and T == 1:
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_reps)
-    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

@@ -1,7 +1,8 @@
 """Build libdsa_indexer.so in-tree with hipcc for gfx950.
 
 ``python -m sparse_attention_kv_indexer_amd.build`` (or ``build()``) compiles
-every HIP source under ``csrc/`` into one shared library next to this file.
+every HIP source under ``csrc/`` into one shared library next to this file,
+and the bench's HBM read probes (``csrc/probe/``) into ``libdsa_probe.so``.
 It needs hipcc but no GPU.
 """
 from __future__ import annotations
@@ -18,6 +19,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "libdsa_indexer.so"
 LIB_PATH = os.path.join(HERE, LIB_NAME)
+PROBE_LIB_PATH = os.path.join(HERE, "libdsa_probe.so")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -46,10 +48,21 @@ def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
+def probe_sources() -> list[str]:
+    return sorted(glob.glob(os.path.join(CSRC, "probe", "*.hip")))
+
+
 def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
-    """Compile the library; returns its path. Always recompiles."""
-    tmp = LIB_PATH + f".tmp{os.getpid()}"
-    cmd = [hipcc(), *FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, "-o", tmp, *sources()]
+    """Compile the library and the probe library; returns the library's path.
+    Always recompiles."""
+    _compile(LIB_PATH, sources(), verbose, extra_flags)
+    _compile(PROBE_LIB_PATH, probe_sources(), verbose, extra_flags)
+    return LIB_PATH
+
+
+def _compile(out: str, srcs: list[str], verbose: bool, extra_flags: list[str] | None) -> None:
+    tmp = out + f".tmp{os.getpid()}"
+    cmd = [hipcc(), *FLAGS, *(extra_flags or []), "-I", INCLUDE, "-I", CSRC, "-o", tmp, *srcs]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -62,8 +75,7 @@ def build(verbose: bool = False, extra_flags: list[str] | None = None) -> str:
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs), flush=True)
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out)
 
 
 if __name__ == "__main__":
