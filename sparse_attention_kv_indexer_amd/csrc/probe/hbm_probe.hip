@@ -24,21 +24,23 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 }
 __device__ __forceinline__ uint32_t fold(u32x4 v) { return v[0] ^ v[1] ^ v[2] ^ v[3]; }
 
-// (a) contiguous read: 16-byte chunk i of the buffer is read by thread i % n_threads.
+// (a) contiguous read: 16-byte chunk i of the buffer is read by thread
+// i % n_threads, kU chunks in flight per thread, with cache policy kPolicy.
+template <int kU, int kPolicy>
 __global__ __launch_bounds__(256) void stream_read(const void* src, uint32_t chunks, uint32_t* out) {
   const rsrc_t r = make_rsrc(src, chunks * 16u);
   const uint32_t n_threads = gridDim.x * blockDim.x;
   const uint32_t t = blockIdx.x * blockDim.x + threadIdx.x;
   uint32_t acc = 0;
   uint32_t i = t;
-  for (; i + 3 * n_threads < chunks; i += 4 * n_threads) {
-    u32x4 v[4];
+  for (; i + (kU - 1) * n_threads < chunks; i += kU * n_threads) {
+    u32x4 v[kU];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, (i + u * n_threads) * 16, 0, kNonTemporal);
+    for (int u = 0; u < kU; ++u) v[u] = __builtin_amdgcn_raw_buffer_load_b128(r, (i + u * n_threads) * 16, 0, kPolicy);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= fold(v[u]);
+    for (int u = 0; u < kU; ++u) acc ^= fold(v[u]);
   }
-  for (; i < chunks; i += n_threads) acc ^= fold(__builtin_amdgcn_raw_buffer_load_b128(r, i * 16, 0, kNonTemporal));
+  for (; i < chunks; i += n_threads) acc ^= fold(__builtin_amdgcn_raw_buffer_load_b128(r, i * 16, 0, kPolicy));
   const rsrc_t o = make_rsrc(out, n_threads * 4u);
   __builtin_amdgcn_raw_buffer_store_b32(acc, o, t * 4, 0, 0);
 }
@@ -90,11 +92,21 @@ __global__ __launch_bounds__(64) void page_read(const void* pool, uint32_t pool_
 }  // namespace
 
 // src: `bytes` of device memory (a multiple of 16, below 4 GiB); out: one
-// uint32 per thread of the grid (grid * 256 words). Returns a hipError_t.
-extern "C" int dsa_probe_stream_read(const void* src, uint64_t bytes, uint32_t* out, int grid, hipStream_t stream) {
+// uint32 per thread of the grid (grid * 256 words); variant 0..3: 4 or 8
+// chunks in flight per thread, streaming or default cache policy. Returns a
+// hipError_t.
+extern "C" int dsa_probe_stream_read(const void* src, uint64_t bytes, uint32_t* out, int grid, int variant,
+                                     hipStream_t stream) {
   if (!src || !out || grid < 1 || bytes % 16 != 0 || bytes == 0 || bytes >= (uint64_t(1) << 32))
     return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(stream_read, dim3(grid), dim3(256), 0, stream, src, (uint32_t)(bytes / 16), out);
+  const uint32_t chunks = (uint32_t)(bytes / 16);
+  switch (variant) {
+    case 0: hipLaunchKernelGGL((stream_read<4, kNonTemporal>), dim3(grid), dim3(256), 0, stream, src, chunks, out); break;
+    case 1: hipLaunchKernelGGL((stream_read<8, kNonTemporal>), dim3(grid), dim3(256), 0, stream, src, chunks, out); break;
+    case 2: hipLaunchKernelGGL((stream_read<4, 0>), dim3(grid), dim3(256), 0, stream, src, chunks, out); break;
+    case 3: hipLaunchKernelGGL((stream_read<8, 0>), dim3(grid), dim3(256), 0, stream, src, chunks, out); break;
+    default: return (int)hipErrorInvalidValue;
+  }
   return (int)hipGetLastError();
 }
 
