@@ -51,11 +51,12 @@
 extern "C" {
 #endif
 
-#define DSA_INDEXER_ABI_VERSION 5
+#define DSA_INDEXER_ABI_VERSION 6
 #define DSA_INDEXER_HEADS 32 /* indexer heads */
 #define DSA_INDEXER_DIM 64   /* head dimension */
 #define DSA_INDEXER_PAGE 64  /* c4 positions per page */
 #define DSA_INDEXER_HIST_BINS 2048 /* bins of the first-digit histogram (score_hist / topk_hist) */
+#define DSA_INDEXER_NOALLOC_SCRATCH_BYTES (64u << 20) /* fixed workspace of dsa_indexer_topk_noalloc, per GPU */
 
 typedef enum {
   DSA_OK = 0,
@@ -64,7 +65,8 @@ typedef enum {
   DSA_ERR_ALIGN = -3,     /* a pointer misses its required alignment */
   DSA_ERR_K = -4,         /* k out of [1, max_c4] */
   DSA_ERR_WORKSPACE = -5, /* workspace too small for the call */
-  DSA_ERR_HIP = -6        /* the HIP runtime reported an error for a launch */
+  DSA_ERR_HIP = -6,       /* the HIP runtime reported an error for a launch */
+  DSA_ERR_SCRATCH = -7    /* sizes beyond the fixed scratch of dsa_indexer_topk_noalloc */
 } dsa_status_t;
 
 /* DSA_INDEXER_ABI_VERSION of the loaded library. */
@@ -184,7 +186,7 @@ int dsa_indexer_score_mtp(const void *q, const float *w, const void *k_pool, int
 
 /* Bytes of device workspace dsa_indexer_topk needs for these sizes: 0 when
  * max_c4 <= 4096 (the workspace may then be NULL) or the sizes are out of
- * range, else batch * ceil(max_c4 / 4096) * (8 + 32768) bytes, about twice the
+ * range, else batch * ceil(max_c4 / 4096) * (32 + 32768) bytes, about twice the
  * logits' own size. */
 size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k);
 
@@ -223,6 +225,31 @@ size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k
 int dsa_indexer_topk(const float *logits, const int32_t *seq_lens, int32_t batch, int32_t max_c4,
                      int32_t k, int32_t *out_idx, float *out_vals, void *workspace,
                      size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Top-k for callers that cannot allocate device memory (code under hipGraph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the result
+ * of dsa_indexer_topk, argument for argument, without the workspace
+ * arguments. The workspace lives in a fixed device array of
+ * DSA_INDEXER_NOALLOC_SCRATCH_BYTES per GPU, part of the library's code object
+ * (held from load until the process ends); the call allocates nothing.
+ *
+ *   - Sizes whose dsa_indexer_topk_workspace_bytes(batch, max_c4, k) exceeds
+ *     DSA_INDEXER_NOALLOC_SCRATCH_BYTES are refused with DSA_ERR_SCRATCH
+ *     (64 MiB: batch * ceil(max_c4 / 4096) up to 2046, e.g. 64 requests of a
+ *     128K-token row width; rows of at most 4096 positions need none).
+ *   - The first call on a device that needs the array resolves its address
+ *     there (hipGetSymbolAddress, no allocation); make that first call
+ *     outside graph capture.
+ *   - Every call on one GPU shares that GPU's array: calls that may overlap
+ *     (other streams, other threads) race and give unspecified positions.
+ *     Calls in stream order are safe; the array needs no clearing between
+ *     them.
+ *
+ * Errors as for dsa_indexer_topk, plus DSA_ERR_SCRATCH.
+ */
+int dsa_indexer_topk_noalloc(const float *logits, const int32_t *seq_lens, int32_t batch, int32_t max_c4,
+                             int32_t k, int32_t *out_idx, float *out_vals, hipStream_t stream);
 
 /*
  * Top-k step over logits written by dsa_indexer_score_hist, with its

@@ -18,7 +18,7 @@ HIST_BINS = 2048  # first-digit histogram of score_hist / topk_hist
 ATT_HEADS, ATT_KD, ATT_VD = 32, 576, 512
 
 _STATUS = {0: "DSA_OK", -1: "DSA_ERR_NULL", -2: "DSA_ERR_SHAPE", -3: "DSA_ERR_ALIGN",
-           -4: "DSA_ERR_K", -5: "DSA_ERR_WORKSPACE", -6: "DSA_ERR_HIP"}
+           -4: "DSA_ERR_K", -5: "DSA_ERR_WORKSPACE", -6: "DSA_ERR_HIP", -7: "DSA_ERR_SCRATCH"}
 
 
 class DsaError(RuntimeError):
@@ -64,6 +64,8 @@ def load() -> ctypes.CDLL:
     lib.dsa_indexer_topk_workspace_bytes.argtypes = [i32, i32, i32]
     lib.dsa_indexer_topk.restype = ctypes.c_int
     lib.dsa_indexer_topk.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, sz, vp]
+    lib.dsa_indexer_topk_noalloc.restype = ctypes.c_int
+    lib.dsa_indexer_topk_noalloc.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp]
     lib.dsa_indexer_sparse_attention_workspace_bytes.restype = sz
     lib.dsa_indexer_sparse_attention_workspace_bytes.argtypes = [i32, i32]
     lib.dsa_indexer_sparse_attention.restype = ctypes.c_int
@@ -295,6 +297,30 @@ def topk(logits, seq_lens, k, out_idx=None, out_vals=None, with_values=False, wo
         _stream_ptr(stream))
     if st != 0:
         raise DsaError(st, "dsa_indexer_topk")
+    return out_idx, out_vals
+
+
+def topk_noalloc(logits, seq_lens, k, out_idx=None, out_vals=None, with_values=False, stream=None):
+    """``topk`` through dsa_indexer_topk_noalloc: the workspace is the
+    library's fixed device array (for callers that cannot allocate; pass
+    ``out_idx`` and ``out_vals`` to allocate nothing here either)."""
+    import torch
+
+    B, N = logits.shape
+    dev = logits.device
+    _check(logits, "logits", (torch.float32,), None)
+    _check(seq_lens, "seq_lens", (torch.int32,), (B,), dev)
+    if out_idx is None:
+        out_idx = torch.empty((B, k), dtype=torch.int32, device=dev)
+    _check(out_idx, "out_idx", (torch.int32,), (B, k), dev)
+    if out_vals is None and with_values:
+        out_vals = torch.empty((B, k), dtype=torch.float32, device=dev)
+    if out_vals is not None:
+        _check(out_vals, "out_vals", (torch.float32,), (B, k), dev)
+    st = load().dsa_indexer_topk_noalloc(logits.data_ptr(), seq_lens.data_ptr(), B, N, k, out_idx.data_ptr(),
+                                         out_vals.data_ptr() if out_vals is not None else None, _stream_ptr(stream))
+    if st != 0:
+        raise DsaError(st, "dsa_indexer_topk_noalloc")
     return out_idx, out_vals
 
 

@@ -8,14 +8,20 @@ namespace {
 
 thread_local int g_last_hip_error = 0;
 
-bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
-bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
+}  // namespace
 
-int from_hip(hipError_t e) {
+int dsa::record_hip_error(hipError_t e) {
   if (e == hipSuccess) return DSA_OK;
   g_last_hip_error = static_cast<int>(e);
   return DSA_ERR_HIP;
 }
+
+namespace {
+
+bool misaligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+bool misaligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) != 0; }
+
+int from_hip(hipError_t e) { return dsa::record_hip_error(e); }
 
 constexpr int32_t kMaxBatch = 65535;  // grid y / x limit used by the launches
 constexpr int32_t kMaxPages = dsa::kMaxRowPositions / dsa::kPage;
@@ -38,6 +44,7 @@ const char* dsa_indexer_status_string(int status) {
     case DSA_ERR_K: return "k out of range (top-k: [1, max_c4]; attention: [1, 2048])";
     case DSA_ERR_WORKSPACE: return "workspace too small";
     case DSA_ERR_HIP: return "HIP runtime error on launch";
+    case DSA_ERR_SCRATCH: return "the sizes need more top-k workspace than the fixed scratch array holds";
     default: return "unknown status";
   }
 }

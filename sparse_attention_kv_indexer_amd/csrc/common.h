@@ -53,6 +53,10 @@ constexpr int kHistShift = 32 - kHistBits;
 // byte range inside one 32-bit buffer range.
 constexpr int32_t kMaxRowPositions = 1 << 28;
 
+// DSA_OK for hipSuccess; otherwise keeps e for dsa_indexer_last_hip_error()
+// on this thread and returns DSA_ERR_HIP.
+int record_hip_error(hipError_t e);
+
 // Enqueue the score kernel (and, with row_hwm, the high-water-mark update).
 // hist: nullptr, or uint32 [B][kHistBins] to which the kernel adds, for every
 // valid position of request b, one count in bin order_key(score) >> kHistShift

@@ -13,7 +13,7 @@ from sparse_attention_kv_indexer_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "dsa_indexer.h")
 
-OK, NULL, SHAPE, ALIGN, K, WS = 0, -1, -2, -3, -4, -5
+OK, NULL, SHAPE, ALIGN, K, WS, SCRATCH = 0, -1, -2, -3, -4, -5, -7
 
 
 def declared_functions():
@@ -29,14 +29,14 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for name in names:
         assert hasattr(lib, name), f"{name} not exported"
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dsa_indexer_abi_version() == 5
-    for st in (OK, NULL, SHAPE, ALIGN, K, WS, -6):
+    assert lib.dsa_indexer_abi_version() == 6
+    for st in (OK, NULL, SHAPE, ALIGN, K, WS, -6, SCRATCH):
         assert lib.dsa_indexer_status_string(st).decode() not in ("", "unknown status")
     assert lib.dsa_indexer_status_string(12345).decode() == "unknown status"
     assert lib.dsa_indexer_last_hip_error() == 0
@@ -236,3 +236,32 @@ def test_w_alignment_matches_the_header(lib, off):
     assert lib.dsa_indexer_score_hist(*score_hist_args(w=A + off)) == ALIGN
     assert lib.dsa_indexer_score_fp8(*score_fp8_args(w=A + off)) == ALIGN
     assert lib.dsa_indexer_score_mtp(*mtp_args(w=A + off)) == ALIGN
+
+
+def noalloc_args(**over):
+    args = dict(logits=A, seq_lens=A, batch=2, max_c4=128, k=16, out_idx=A, out_vals=None, stream=None)
+    args.update(over)
+    return list(args.values())
+
+
+@pytest.mark.parametrize("over,want", [(dict(logits=None), NULL), (dict(seq_lens=None), NULL),
+                                       (dict(out_idx=None), NULL), (dict(batch=0), SHAPE),
+                                       (dict(max_c4=0), SHAPE), (dict(max_c4=(1 << 28) + 1, k=1), SHAPE),
+                                       (dict(k=0), K), (dict(k=129), K), (dict(out_idx=A + 2), ALIGN),
+                                       (dict(out_vals=A + 1), ALIGN), (dict(logits=A + 3), ALIGN),
+                                       (dict(batch=64, max_c4=4096 * 32, k=64), SCRATCH),
+                                       (dict(batch=2048, max_c4=4097, k=64), SCRATCH)])
+def test_topk_noalloc_rejects(lib, over, want):
+    """Host-side refusals of the allocation-free top-k, sizes past its fixed
+    array included (64 MiB: at most 2046 segment slots of 4096 positions)."""
+    assert lib.dsa_indexer_topk_noalloc(*noalloc_args(**over)) == want
+
+
+def test_topk_noalloc_limit_matches_the_header(lib):
+    text = open(HEADER).read()
+    assert "#define DSA_INDEXER_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
+    per_slot = 32 + 32768  # a segment's record, then its (key, position) pairs
+    assert "* (32 + 32768) bytes" in text and "up to 2046" in text
+    assert lib.dsa_indexer_topk_workspace_bytes(2046, 4097, 64) == 2046 * 2 * per_slot
+    assert lib.dsa_indexer_topk_workspace_bytes(2046, 4096, 64) == 0
+    assert 2046 * per_slot <= (64 << 20) < 2047 * per_slot

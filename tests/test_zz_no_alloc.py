@@ -1,0 +1,75 @@
+"""The allocation-free top-k (dsa_indexer_topk_noalloc) through the C ABI:
+its output equals dsa_indexer_topk's with a caller workspace, bit for bit,
+on two calls in a row, the second with a smaller input, and on random rows
+that exercise its whole-row fallback. Sizes past its fixed array are refused
+on the host."""
+import numpy as np
+import pytest
+
+from gpu_helpers import check_topk_exact, run_score, say
+from sparse_attention_kv_indexer_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+def _both(lib, logits, lens, k):
+    import torch
+
+    B = logits.shape[0]
+    ref_i = torch.full((B, k), -7, dtype=torch.int32, device=logits.device)
+    ref_v = torch.full((B, k), 7.0, dtype=torch.float32, device=logits.device)
+    got_i = torch.full((B, k), -9, dtype=torch.int32, device=logits.device)
+    got_v = torch.full((B, k), 9.0, dtype=torch.float32, device=logits.device)
+    lib.topk(logits, lens, k, out_idx=ref_i, out_vals=ref_v)
+    lib.topk_noalloc(logits, lens, k, out_idx=got_i, out_vals=got_v)
+    torch.cuda.synchronize()
+    return ref_i.cpu().numpy(), ref_v.cpu().numpy(), got_i.cpu().numpy(), got_v.cpu().numpy()
+
+
+def _same(ref_i, ref_v, got_i, got_v):
+    assert np.array_equal(ref_i, got_i), "indices differ from dsa_indexer_topk"
+    assert np.array_equal(ref_v.view(np.uint32), got_v.view(np.uint32)), "values differ from dsa_indexer_topk"
+
+
+def test_noalloc_equals_topk_on_two_calls_in_a_row(lib):
+    # the first call leaves the array holding c3's segments; the second, smaller
+    # input (c2: shorter rows, fewer requests) must not be affected by them
+    for name in ("c3", "c2"):
+        say(f"topk_noalloc vs topk on {name}")
+        inp = wl.generate(name)
+        got, t, out = run_score(lib, inp)
+        ref_i, ref_v, got_i, got_v = _both(lib, out, t["seq_lens"], inp.topk)
+        _same(ref_i, ref_v, got_i, got_v)
+        check_topk_exact(got_i, got_v, got, inp.seq_lens, inp.topk)
+
+
+def test_noalloc_whole_row_paths(lib):
+    """Rows of ties and NaN that take the whole-row select, after a call that
+    filled the array with other candidates."""
+    import torch
+
+    rng = np.random.default_rng(17)
+    B, N, k = 8, 20000, 300
+    x = rng.standard_normal((B, N)).astype(np.float32)
+    x[1] = 2.0                      # all equal: more candidates than a workgroup holds
+    x[2, ::3] = np.nan
+    x[3] = np.round(x[3] * 4) / 4   # heavy ties
+    lens = np.array([20000, 20000, 19999, 12345, 4097, 4096, 300, 0], np.int32)
+    say("topk_noalloc whole-row paths")
+    xd = torch.from_numpy(x).cuda()
+    ld = torch.from_numpy(lens).cuda()
+    ref_i, ref_v, got_i, got_v = _both(lib, xd, ld, k)
+    _same(ref_i, ref_v, got_i, got_v)
+    check_topk_exact(got_i, got_v, x, lens, k)
+
+
+def test_noalloc_refuses_sizes_past_the_array(lib):
+    import torch
+
+    load = lib.load()
+    limit = 64 << 20
+    B, N = 64, 4096 * 64  # 4096 segment slots: twice what the array holds
+    assert load.dsa_indexer_topk_workspace_bytes(B, N, 64) > limit
+    logits = torch.empty((1, 16), dtype=torch.float32, device="cuda")  # never read: refused first
+    st = load.dsa_indexer_topk_noalloc(logits.data_ptr(), logits.data_ptr(), B, N, 64, logits.data_ptr(), None, None)
+    assert st == -7 and "scratch" in lib.status_string(st)
