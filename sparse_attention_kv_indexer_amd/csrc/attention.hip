@@ -139,7 +139,11 @@ __device__ __forceinline__ void att_place(int nsplit, int& b, int& s) {
 // not track it: its completion is awaited explicitly (s_waitcnt vmcnt, then a
 // barrier) before any wave reads the buffer. Extra outstanding loads can only
 // make the compiler's own vmcnt waits stricter, never looser. m0 is listed as
-// clobbered, so the compiler keeps no value of its own there across the load.
+// clobbered, so the compiler keeps no value of its own there across the load
+// (it reserves m0 and warns that a reserved register is named; the warning is
+// silenced here only).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
   asm volatile(
       "s_mov_b32 m0, %1\n\t"
@@ -149,6 +153,7 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
       : "v"(src), "s"(lds)
       : "memory", "m0");
 }
+#pragma clang diagnostic pop
 
 // Encoding of s_waitcnt that waits until at most n vector-memory operations
 // and no LDS operations of this wave are outstanding.
