@@ -18,7 +18,7 @@
 // workgroup gets pages (a workgroup scores its pages, then writes its tail
 // chunks: writes between the page reads slow the read stream), and splits the
 // two lists as one otherwise (the workgroups past the pages take the tail).
-// The launch shape
+// The grid holds eight workgroups per compute unit. The launch shape
 // depends only on (batch, max_pages), so it can be captured once and replayed
 // for any lengths, and the work and HBM traffic follow the actual lengths:
 // pages past a length are never read (the early exit of the section "The
@@ -175,13 +175,15 @@ __device__ __forceinline__ int lds_slot8(int row, int j) { return row * 8 + (j ^
 
 // kTok query tokens per request (1: a plain decode step; more: the current
 // token and draft tokens, each with its own causal length), every key page
-// read once for all of them. More tokens hold more query registers, hence
-// fewer resident waves.
-template <int kTok>
-constexpr int waves_per_simd() { return kTok == 1 ? 3 : 2; }
+// read once for all of them. Two resident waves per SIMD, measured against
+// three: fewer, longer ranges write their logits in fewer, larger bursts,
+// which slow the read stream less (bf16 keys: c3 -1.0 us, full -1.1 us; fp8
+// keys: c3 -0.6 us, full -1.2 us).
+template <bool kFp8, int kTok>
+constexpr int waves_per_simd() { return 2; }
 
 template <bool kFp8, int kTok>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<kTok>(), waves_per_simd<kTok>())))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(waves_per_simd<kFp8, kTok>(), waves_per_simd<kFp8, kTok>())))
 void score_kernel(
     const uint16_t* __restrict__ q,          // bf16 [B][kTok][32][64]
     const float* __restrict__ w,             // [B][kTok][32]
@@ -237,14 +239,15 @@ void score_kernel(
 
   // bf16 keys: a page's 64 scores (per query token) go to an LDS stash,
   // written out as runs of contiguous logits at the end of the workgroup's
-  // pages (or when the stash is full) with 1 KiB wave stores. Measured with
-  // a load probe over random 8 KiB pages: 256 B of results stored after every
-  // page cost the read stream 6 us of 48 at 32768 pages; the same bytes
-  // written in one burst per workgroup cost 2. (Measured in the kernel: full
-  // 50.2 -> 48.4 us; two and three query tokens 1-2 us per step faster; fp8
-  // pages and four query tokens no gain, so they store per page.)
+  // pages (or when the stash is full) with 1 KiB streaming wave stores.
+  // Measured with a load probe over random 8 KiB pages: 256 B of results
+  // stored after every page cost the read stream 6 us of 48 at 32768 pages;
+  // the same bytes written in one burst per workgroup cost 2. (Measured in
+  // the kernel: full 50.2 -> 48.4 us; two and three query tokens 1-2 us per
+  // step faster; fp8 pages and four query tokens no gain, so they store per
+  // page. Streaming stores for the bursts: -0.3 to -0.5 us.)
   constexpr bool kStashed = !kFp8 && kTok <= 3;
-  constexpr int kStash = kTok == 1 ? 16 : 8;  // pages; token t's rows at [t][page][64]
+  constexpr int kStash = kTok == 1 ? 32 : 8;  // pages; token t's rows at [t][page][64]
   __shared__ __attribute__((aligned(16))) uint32_t stash[kStashed ? kTok * kStash * kPage : 4];
   __shared__ int stash_b[kStash], stash_j[kStash];
   int stash_n = 0;
@@ -265,7 +268,7 @@ void score_kernel(
                                      (uint32_t)words * 4u);
         for (int w0 = lane * 4; w0 < words; w0 += 256)
           __builtin_amdgcn_raw_buffer_store_b128(
-              *reinterpret_cast<const u32x4*>(&stash[(t * kStash + p) * kPage + w0]), out, w0 * 4, 0, 0);
+              *reinterpret_cast<const u32x4*>(&stash[(t * kStash + p) * kPage + w0]), out, w0 * 4, 0, kNonTemporal);
       }
       p = q;
     }
@@ -574,7 +577,7 @@ hipError_t launch_score(const void* q, const float* w, const void* k_pool, const
   // list these shapes allow (every slot a page, plus every tail chunk)
   const int64_t width = (int64_t)max_pages * kPage;
   const int64_t most = (int64_t)batch * max_pages + (int64_t)batch * ((width + kTailChunk - 1) / kTailChunk);
-  const int per_cu = 4 * (tokens == 1 ? waves_per_simd<1>() : waves_per_simd<2>());
+  const int per_cu = 4 * (k_scale != nullptr ? waves_per_simd<true, 1>() : waves_per_simd<false, 1>());
   const int grid = (int)std::min<int64_t>((int64_t)cu_count(stream) * per_cu, most);
   if (k_scale != nullptr) {
     launch_variant<true, 1>(grid, stream, q, w, k_pool, k_scale, num_pages, page_table, seq_lens, batch, max_pages,
