@@ -8,11 +8,14 @@
 // max_pages * 64 positions.
 //
 // Work lists. The work of one call is two flat lists: every valid page of
-// every request (request-major, page-minor), and the -inf tail of every
-// request cut into chunks of kTailChunk positions. The tail of a request runs
-// from its first page past the length to the row end (stateless mode) or to
-// the page holding its previous high-water mark (incremental mode, where
-// everything beyond is -inf already). A fixed grid of one-wave workgroups, as
+// every request (request-major, page-minor), and the -inf tails. In the
+// stateless mode the tail of a request runs from its first page past the
+// length to the row end, cut into chunks of kTailChunk positions. In the
+// incremental mode each request's tail is one item: the wave that takes it
+// reads the request's previous high-water mark, rewrites -inf only up to the
+// page holding it (everything beyond is -inf already) and then stores the new
+// mark; no other wave reads that mark, so the update needs no second kernel.
+// A fixed grid of one-wave workgroups, as
 // many as the chip keeps resident (capped by the largest list the shapes
 // allow), splits each list into equal contiguous ranges when every
 // workgroup gets pages (a workgroup scores its pages, then writes its tail
@@ -87,10 +90,11 @@ struct Shape {
 };
 
 // Request b's share of the work: its valid pages (those below the longest of
-// its tokens' lengths), and the positions [tail0, tail1) of its -inf tail in
-// chunks of kTailChunk.
+// its tokens' lengths, len), and its -inf tail from position tail0: chunks of
+// kTailChunk up to the row end (stateless mode), or one item (incremental
+// mode). Reads the lengths only, never the marks.
 struct RowWork {
-  uint32_t pages, chunks, tail0, tail1;
+  uint32_t pages, chunks, tail0, len;
 };
 __device__ __forceinline__ RowWork row_work(const Shape& sh, int b) {
   RowWork r{0, 0, 0, 0};
@@ -98,16 +102,10 @@ __device__ __forceinline__ RowWork row_work(const Shape& sh, int b) {
     int len = 0;
     for (int t = 0; t < sh.tok; ++t)
       len = max(len, clamp_len((int)__builtin_amdgcn_raw_buffer_load_b32(sh.lens, (b * sh.tok + t) * 4, 0, 0), sh.width));
+    r.len = (uint32_t)len;
     r.pages = (uint32_t)((len + kPage - 1) / kPage);
     r.tail0 = r.pages * kPage;
-    r.tail1 = (uint32_t)sh.width;
-    if (sh.incremental) {
-      // beyond the page holding the old mark everything is -inf already
-      const uint32_t hw =
-          (uint32_t)clamp_len((int)__builtin_amdgcn_raw_buffer_load_b32(sh.marks, b * 4, 0, 0), sh.width);
-      r.tail1 = max(r.tail0, (hw + kPage - 1) / kPage * kPage);
-    }
-    r.chunks = (r.tail1 - r.tail0 + kTailChunk - 1) / kTailChunk;
+    r.chunks = sh.incremental ? 1u : ((uint32_t)sh.width - r.tail0 + kTailChunk - 1) / kTailChunk;
   }
   return r;
 }
@@ -194,14 +192,18 @@ void score_kernel(
     const int32_t* __restrict__ seq_lens,    // [B][kTok]
     int32_t batch, int32_t max_pages,
     float* __restrict__ logits,              // [B][kTok][max_pages * 64]
-    const int32_t* __restrict__ row_hwm,     // [B] or null (kTok == 1 only)
+    int32_t* __restrict__ row_hwm,           // [B] or null (kTok == 1 only)
     uint32_t* __restrict__ hist)             // [B][kHistBins] or null (kTok == 1 only)
 {
   const int lane = threadIdx.x;
   const int half = lane >> 5;
   const int n = lane & 31;
+  // (the marks' resource is built from row_hwm alone, empty without it: were
+  // it able to point at seq_lens, the stores of the new marks would keep the
+  // compiler from reading the lengths through scalar loads, and the vector
+  // loads it would use instead wait for every page load in flight)
   const Shape sh{make_rsrc(seq_lens, (uint32_t)(batch * kTok) * 4u),
-                 make_rsrc(row_hwm != nullptr ? row_hwm : seq_lens, (uint32_t)batch * 4u),
+                 make_rsrc(row_hwm, row_hwm != nullptr ? (uint32_t)batch * 4u : 0u),
                  kTok == 1 && row_hwm != nullptr, batch, max_pages * kPage, kTok};
 
   // list totals, then this workgroup's contiguous ranges: pages [s, pe) and
@@ -513,7 +515,15 @@ void score_kernel(
       uint32_t c;
       window_find(W, it, sh, true, b, c);
       const RowWork r = row_work(sh, b);
-      const uint32_t c0 = r.tail0 + c * kTailChunk, c1 = min(r.tail1, c0 + kTailChunk);
+      uint32_t c0 = r.tail0 + c * kTailChunk, c1 = min((uint32_t)sh.width, c0 + kTailChunk);
+      if (sh.incremental) {
+        // this wave owns request b's mark: the tail is [tail0, page of the old
+        // mark), and the new mark is stored after the old one was read
+        const uint32_t old = (uint32_t)clamp_len((int)__builtin_amdgcn_raw_buffer_load_b32(sh.marks, b * 4, 0, 0), sh.width);
+        c0 = r.tail0;
+        c1 = max(r.tail0, (old + kPage - 1) / kPage * kPage);
+        if (lane == 0) __builtin_amdgcn_raw_buffer_store_b32(r.len, sh.marks, b * 4, 0, 0);
+      }
 #pragma unroll
       for (int t = 0; t < kTok; ++t) {
         const rsrc_t row = make_rsrc(logits + ((int64_t)b * kTok + t) * sh.width, (uint32_t)sh.width * 4u);
@@ -524,17 +534,6 @@ void score_kernel(
           __builtin_amdgcn_raw_buffer_store_b128(ninf, row, p * 4, 0, kNonTemporal);
       }
     }
-  }
-}
-
-__global__ __launch_bounds__(256) void hwm_kernel(const int32_t* __restrict__ seq_lens, int32_t batch,
-                                                   int32_t width, int32_t* __restrict__ row_hwm) {
-  const int b = blockIdx.x * blockDim.x + threadIdx.x;
-  const rsrc_t lens = make_rsrc(seq_lens, batch * sizeof(int32_t));
-  const rsrc_t marks = make_rsrc(row_hwm, batch * sizeof(int32_t));
-  if (b < batch) {
-    const int len = (int)__builtin_amdgcn_raw_buffer_load_b32(lens, b * 4, 0, 0);
-    __builtin_amdgcn_raw_buffer_store_b32((uint32_t)clamp_len(len, width), marks, b * 4, 0, 0);
   }
 }
 
@@ -601,11 +600,6 @@ hipError_t launch_score(const void* q, const float* w, const void* k_pool, const
                                  max_pages, logits, nullptr, nullptr);
         break;
     }
-  }
-  if (row_hwm != nullptr && tokens == 1) {
-    // after every workgroup of the score kernel has read the old marks
-    hipLaunchKernelGGL(hwm_kernel, dim3((batch + 255) / 256), dim3(256), 0, stream, seq_lens, batch,
-                       max_pages * kPage, row_hwm);
   }
   return hipGetLastError();
 }
