@@ -76,6 +76,8 @@ constexpr int kRound = 256;                   // sub-slot records per gather rou
 constexpr int kSpecSlots = 32;                // sub-slots read before their counts are known
 constexpr int kSpec = 256;                    // pairs read ahead per such sub-slot
 constexpr int kSweep = 16 * kRowThreads;      // positions per block of the whole-row output sweep
+constexpr int kSmall = 64;                    // keys of a bin that one wave ranks directly
+constexpr int kSmallRanged = 16;              // the same, in the ranged select over long rows' candidates
 
 static_assert(kSegWaves * 64 == kSegThreads && kPerLane * kSegThreads == kSeg, "segment work split");
 static_assert(2 * kRowThreads * 4 == kSpecSlots * kSpec, "read-ahead: four 16-byte loads per lane");
@@ -172,6 +174,7 @@ __device__ __forceinline__ void block_scan2(uint32_t& a, uint32_t& b, uint32_t* 
 // kNB / 64 * l), so no barrier or broadcast follows.
 struct Pick {
   uint32_t bin, above;
+  bool ok;  // false: the histogram holds fewer keys than the rank asked for
 };
 // load4(q, b) returns bins b .. b + 3 (b = the lane's lowest bin + 4 q).
 template <int kNB>
@@ -204,7 +207,7 @@ __device__ __forceinline__ Pick wave_pick(Load4 load4, RankOf rank_of) {
   const uint32_t rank = rank_of(total);
   const uint32_t excl = incl - s;
   const uint64_t hit = __ballot(excl < rank && rank <= incl);
-  if (hit == 0) return Pick{0u, total};
+  if (hit == 0) return Pick{0u, total, false};
   const int src = __builtin_ctzll(hit);
   // in the lane holding it: the chunk, top chunk first, then the bin
   uint32_t acc = excl, above_q = 0;
@@ -237,7 +240,8 @@ __device__ __forceinline__ Pick wave_pick(Load4 load4, RankOf rank_of) {
     }
     acc += e4[e];
   }
-  return Pick{(uint32_t)__builtin_amdgcn_readlane((int)bin, src), (uint32_t)__builtin_amdgcn_readlane((int)above, src)};
+  return Pick{(uint32_t)__builtin_amdgcn_readlane((int)bin, src), (uint32_t)__builtin_amdgcn_readlane((int)above, src),
+              true};
 }
 
 // wave_pick over a histogram in LDS (bins at hslot positions).
@@ -408,8 +412,10 @@ struct RowShared {
   uint32_t off[kRound];   //   its first candidate
   uint32_t roff[kRound];  //   its first pair not read ahead, in the round's list of those
   uint32_t part[2 * kRowWaves];
-  uint32_t bcast[2];
-  uint32_t hpick[2];  // from the score kernel's histogram: bin of the k-th largest, count above it
+  uint32_t bcast[3];
+  uint32_t hpick[3];  // from the score kernel's histogram: bin of the k-th largest, count above it, found
+  uint32_t small[kSmall];  // the keys of the last bin, once at most kSmall remain
+  uint32_t small_n;
   uint32_t range[2];  // candidates at or above the largest cut, largest candidate key
   uint32_t max_cut;
 };
@@ -437,8 +443,9 @@ __device__ __forceinline__ void clear_hists() {
 // Resolves one digit: counts the keys matching (T, mask) into pass's
 // histogram with `count`; wave 0 picks the digit of the k-th largest and
 // hands it to the others through LDS.
+// Returns how many keys match the resolved digits (the count in the chosen bin).
 template <int kPass, typename Count>
-__device__ __forceinline__ void radix_pass(uint32_t& T, uint32_t& mask, uint32_t& remaining, Count count) {
+__device__ __forceinline__ uint32_t radix_pass(uint32_t& T, uint32_t& mask, uint32_t& remaining, Count count) {
   constexpr int shift = kPass == 0 ? 21 : (kPass == 1 ? 10 : 0);
   constexpr uint32_t dmask = kPass == 2 ? 0x3FFu : 0x7FFu;
   uint32_t* h = pass_hist(kPass);
@@ -449,6 +456,7 @@ __device__ __forceinline__ void radix_pass(uint32_t& T, uint32_t& mask, uint32_t
     if (threadIdx.x == 0) {
       rs.bcast[0] = p.bin;
       rs.bcast[1] = p.above;
+      rs.bcast[2] = h[hslot(p.bin)];
     }
   }
   __syncthreads();
@@ -456,6 +464,47 @@ __device__ __forceinline__ void radix_pass(uint32_t& T, uint32_t& mask, uint32_t
   T |= rs.bcast[0] << shift;
   remaining -= rs.bcast[1];
   mask |= dmask << shift;
+  return rs.bcast[2];
+}
+
+// Ends a select over a short candidate set once at most kSmall candidates
+// match the digits resolved so far (the keys of the bin holding the k-th
+// largest; `remaining` of them, 1 <= remaining <= their count, belong to the
+// top k), instead of the radix passes left: the keys of the bin are collected
+// in LDS and wave 0 ranks them, one per lane, against each other. match(key)
+// tells a key of the bin. Every lane must call it. (Measured on rows of at most
+// 4096 positions: top-k 5.4 -> 5.0 us at 64 requests of 128 positions; on the
+// longer rows' ranged select it was slower, so that select keeps its passes.)
+template <typename Match>
+__device__ __forceinline__ void finish_small(int n, uint32_t remaining, Match match, uint32_t& T, uint32_t& r) {
+  const int tid = threadIdx.x;
+  if (tid == 0) rs.small_n = 0u;
+  __syncthreads();
+  for (int i = tid; i < n; i += kRowThreads) {
+    const uint32_t kk = rs.cand_key[i];
+    if (match(kk)) rs.small[atomicAdd(&rs.small_n, 1u)] = kk;  // exactly the bin's count, <= kSmall
+  }
+  __syncthreads();
+  if ((tid >> 6) == 0) {
+    const int m = __builtin_amdgcn_readfirstlane((int)rs.small_n);
+    const uint32_t mine = tid < m ? rs.small[tid] : 0u;
+    uint32_t gt = 0u, ge = 0u;  // keys of the bin above / at or above this lane's
+    for (int i = 0; i < m; ++i) {
+      const uint32_t v = (uint32_t)__builtin_amdgcn_readlane((int)mine, i);
+      gt += v > mine ? 1u : 0u;
+      ge += v >= mine ? 1u : 0u;
+    }
+    // the remaining-th largest: fewer than `remaining` keys above it, at least that many at or above
+    const uint64_t hit = __ballot(tid < m && gt < remaining && ge >= remaining);
+    const int src = hit ? __builtin_ctzll(hit) : 0;
+    if (tid == 0) {
+      rs.bcast[0] = (uint32_t)__builtin_amdgcn_readlane((int)mine, src);
+      rs.bcast[1] = remaining - (uint32_t)__builtin_amdgcn_readlane((int)gt, src);
+    }
+  }
+  __syncthreads();
+  T = rs.bcast[0];
+  r = rs.bcast[1];
 }
 
 // Exact radix select over the n candidates in LDS (n >= k): the k-th largest
@@ -485,8 +534,18 @@ __device__ __forceinline__ Kth select_candidates(int n, int k, bool from_hist, u
       if ((kk & mask) == T) atomicAdd(&h[hslot((kk >> shift) & dmask)], 1u);
     }
   };
-  if (!from_hist) radix_pass<0>(T, mask, remaining, count);
-  radix_pass<1>(T, mask, remaining, count);
+  auto in_bin = [&](uint32_t kk) { return (kk & mask) == T; };
+  uint32_t r;
+  if (!from_hist) {
+    if (radix_pass<0>(T, mask, remaining, count) <= (uint32_t)kSmall) {
+      finish_small(n, remaining, in_bin, T, r);
+      return Kth{T, r};
+    }
+  }
+  if (radix_pass<1>(T, mask, remaining, count) <= (uint32_t)kSmall) {
+    finish_small(n, remaining, in_bin, T, r);
+    return Kth{T, r};
+  }
   radix_pass<2>(T, mask, remaining, count);
   return Kth{T, remaining};
 }
@@ -547,13 +606,21 @@ __device__ __noinline__ Kth select_candidates_ranged(int n, int k, uint32_t base
       if (tid == 0) {
         rs.bcast[0] = p.bin;
         rs.bcast[1] = p.above;
+        rs.bcast[2] = h[hslot(p.bin)];
       }
     }
     __syncthreads();
     prefix = (prefix << width) | rs.bcast[0];
     remaining -= rs.bcast[1];
     top = low;
+    const uint32_t in_bin = rs.bcast[2];
     // (bcast is written again only after the next pass's first barrier)
+    if (top > 0 && in_bin <= (uint32_t)kSmallRanged) {
+      uint32_t T, r;
+      finish_small(n, remaining, [&](uint32_t kk) {
+        return kk >= base && (uint32_t)((uint64_t)(kk - base) >> top) == prefix; }, T, r);
+      return Kth{T, r};
+    }
   }
   return Kth{base + prefix, remaining};
 }
@@ -778,6 +845,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     if (tid == 0) {
       rs.hpick[0] = p.bin;
       rs.hpick[1] = p.above;
+      rs.hpick[2] = p.ok ? 1u : 0u;
     }
   }
   clear_hists();
@@ -800,15 +868,31 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     n = gather_segments(ws, b, (int)gridDim.x, n_seg, len);
   }
   __syncthreads();
-  const bool from_hist = hist != nullptr;
+  bool from_hist = hist != nullptr && rs.hpick[2] != 0u;
   uint32_t bin0 = 0u, above0 = 0u;
-  if (from_hist) {
+  if (hist != nullptr) clear_hist_row();  // wave 0 read it before the barrier
+  if (from_hist && n >= k) {
+    // The histogram is taken only where the candidates confirm it: fewer than
+    // k of them above its bin and at least k in or above it. The candidates
+    // hold every key at or above the bin's lower edge (each segment cut there;
+    // a short row is all candidates), so these counts are exact, and the
+    // count above comes from them: counts that do not belong to these logits
+    // cannot change the result.
     bin0 = rs.hpick[0];
-    above0 = rs.hpick[1];
-    clear_hist_row();  // wave 0 read it before the barrier
+    uint32_t ab = 0u, ge = 0u, tot_ab, tot_ge;
+    for (int i = tid; i < n; i += kRowThreads) {
+      const uint32_t d = rs.cand_key[i] >> 21;
+      ab += d > bin0 ? 1u : 0u;
+      ge += d >= bin0 ? 1u : 0u;
+    }
+    block_scan2<kRowWaves>(ab, ge, rs.part, &tot_ab, &tot_ge);
+    from_hist = tot_ab < (uint32_t)k && tot_ge >= (uint32_t)k;
+    above0 = tot_ab;
   }
   if (n >= k) {  // n < 0: more than kCap candidates
     // gathered candidates: the select over those at or above the largest cut
+    // (with a histogram that the candidates did not confirm, the ranged select
+    // over the candidates at or above the largest cut decides, as without one)
     const Kth t = (!from_hist && len > kSeg) ? select_candidates_ranged(n, k, rs.max_cut)
                                              : select_candidates(n, k, from_hist, bin0, above0);
     // every key a segment left out lies below its cut, hence below T

@@ -162,3 +162,36 @@ def test_graph_replays_reset_the_histogram(lib):
         eager = lib.score(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"])
         torch.cuda.synchronize()
         assert np.array_equal(eager.cpu().numpy().view(np.uint32), got.view(np.uint32)), rep
+
+
+@pytest.mark.parametrize("name", ["c2", "c3"])
+def test_histogram_that_does_not_belong_to_the_logits(lib, name):
+    """topk_hist with a histogram that is not the one score_hist counted for
+    these logits: all zero (a second topk_hist on the same logits, after the
+    first set it back to zero), counts piled into one wrong bin, and counts
+    shifted by one bin. The result must still equal the oracle's top-k on the
+    same scores, on rows shorter and longer than one segment and around k."""
+    import torch
+
+    say(f"topk_hist with foreign histograms {name}")
+    inp = wl.generate(name)
+    lens = inp.seq_lens.copy()
+    k = inp.topk
+    lens[:4] = [k + 1, min(4096, inp.max_c4), k - 1, 4097 if inp.max_c4 > 4097 else inp.max_c4]
+    inp.seq_lens[:] = np.clip(lens, 0, inp.max_c4)
+    t = lib.to_device(inp)
+    hist = lib.hist_buffer(inp.batch)
+    logits, h, idx, vals = _fused(lib, t, inp, hist, k)
+    got = _check_all(lib, t, inp, k, logits, h, idx, vals, hist)
+    wrong = [np.zeros_like(h)]
+    pile = np.zeros_like(h)
+    pile[:, 1900] = 10 * k  # far above every score's bin
+    wrong.append(pile)
+    wrong.append(np.roll(h, 3, axis=1))  # the right counts, three bins too high
+    wrong.append(np.roll(h, -3, axis=1))  # three bins too low
+    for w in wrong:
+        hist.copy_(torch.from_numpy(w.view(np.int32)).to(hist.device))
+        i2, v2 = lib.topk(logits, t["seq_lens"], k, with_values=True, hist=hist)
+        torch.cuda.synchronize()
+        check_topk_exact(i2.cpu().numpy(), v2.cpu().numpy(), got, inp.seq_lens, k)
+        assert not hist.any().item(), "the top-k left the histogram non-zero"
