@@ -236,8 +236,9 @@ def timed_batches(launch, n: int, batches: int = BATCHES):
 
 def probes(page_counts, cu_count: int) -> dict:
     """Achievable HBM read rates on this GPU: a 1 GiB contiguous read, and
-    random 8 KiB pages from a 512 MiB pool for each page count (the valid
-    pages of a workload), on the score kernel's grid of one-wave workgroups."""
+    random 8 KiB pages from a 1 GiB pool for each page count (the valid pages
+    of a workload), on the score kernel's grid of one-wave workgroups, with
+    disjoint page sets read round robin."""
     import numpy as np
     import torch
 
@@ -272,25 +273,29 @@ def probes(page_counts, cu_count: int) -> dict:
                           "shape": f"{per_cu} x 256 lanes per CU, {8 if variant & 1 else 4} loads in flight per lane, "
                                    f"{'default' if variant >= 2 else 'streaming'} cache policy"}
     del src
-    pool_pages = 65536  # 512 MiB of 8 KiB pages: twice the Infinity Cache
+    pool_pages = 131072  # 1 GiB of 8 KiB pages: four times the Infinity Cache
     pool = torch.empty(pool_pages * 8192, dtype=torch.uint8, device="cuda").fill_(3)
     grid_p = cu_count * 12  # the score kernel's grid
     outp = torch.empty(grid_p * 64, dtype=torch.int32, device="cuda")
     rng = np.random.default_rng(0)
     for name, n in page_counts.items():
-        ids_np = rng.permutation(pool_pages)[:n].astype(np.int32)
-        assert 0 < n <= pool_pages and ids_np.min() >= 0 and ids_np.max() < pool_pages
-        ids = torch.from_numpy(ids_np).cuda()
+        # R disjoint random page sets, read round robin (as the bench rotates its
+        # input copies), so that no launch finds its pages in the Infinity Cache
+        R = min(16, max(2, math.ceil(2 * MALL_BYTES / (n * 8192))))
+        assert 0 < n and R * n <= pool_pages
+        perm = rng.permutation(pool_pages)[:R * n].astype(np.int32)
+        assert perm.min() >= 0 and perm.max() < pool_pages
+        sets = [torch.from_numpy(perm[r * n:(r + 1) * n].copy()).cuda() for r in range(R)]
 
-        def page_launch(_):
-            rc = lib.dsa_probe_page_read(pool.data_ptr(), pool_pages * 8192, ids.data_ptr(), n, outp.data_ptr(),
-                                         grid_p, st)
+        def page_launch(i):
+            rc = lib.dsa_probe_page_read(pool.data_ptr(), pool_pages * 8192, sets[i % R].data_ptr(), n,
+                                         outp.data_ptr(), grid_p, st)
             assert rc == 0, rc
 
-        for _ in range(3):
-            page_launch(0)
-        ms = timed_batches(page_launch, 20)
-        res[f"page_read_{name}"] = {"pages": n, "bytes": n * 8192, "us": round(ms * 1e3, 2),
+        for i in range(2 * R):
+            page_launch(i)
+        ms = timed_batches(page_launch, 20 * R)
+        res[f"page_read_{name}"] = {"pages": n, "bytes": n * 8192, "page_sets": R, "us": round(ms * 1e3, 2),
                                     "GBs": round(n * 8192 / (ms * 1e-3) / 1e9, 1)}
     torch.cuda.synchronize()
     return res
@@ -308,10 +313,13 @@ def cu_count() -> int:
 
 def measure_step(cfg_name: str, steps: int, warmup: int, hwm=False, keys="bf16", T=1, fused=False, rotate=0,
                  inp=None) -> dict:
-    """One workload: R input copies, one captured graph of [score; top-k]
-    per copy, `warmup` untimed replays, then exactly `steps` timed replays in
-    BATCHES batches (events between batches, no synchronization), and the
-    median per-launch duration of the score and top-k calls alone."""
+    """One workload: R input copies and one captured graph of R consecutive
+    steps [score; top-k], one per copy (as a decode step's graph holds the
+    indexer of consecutive layers, each over its own keys), `warmup` untimed
+    steps, then exactly `steps` timed steps in BATCHES batches (events between
+    batches, no synchronization), and the median per-launch duration of the
+    score and top-k calls alone. Also times one-step graphs, whose replay
+    overhead is reported beside the step."""
     import numpy as np
     import torch
 
@@ -369,34 +377,48 @@ def measure_step(cfg_name: str, steps: int, warmup: int, hwm=False, keys="bf16",
         launch_step(t)
     torch.cuda.synchronize()
 
-    # one captured graph per input copy: [score; top-k]
-    graphs = []
+    # graphs: all R steps (one per input copy), and the first r of them for
+    # the remainder of `steps`; one-step graphs for the replay overhead
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
-    for t in sets:
+
+    def capture(ts):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=cap):
-            launch_step(t)
-        graphs.append(g)
+            for t in ts:
+                launch_step(t)
+        return g
+
+    g_all = capture(sets)
+    rem = steps % R
+    g_rem = capture(sets[:rem]) if rem else None
+    g_one = [capture([t]) for t in sets]
     torch.cuda.synchronize()
 
-    for i in range(warmup):
-        graphs[i % R].replay()
+    for _ in range(-(-warmup // R)):
+        g_all.replay()
     torch.cuda.synchronize()
-    # exactly `steps` replays between one synchronized start and end, with
+    # exactly `steps` steps between one synchronized start and end, with
     # events at the batch boundaries only
-    cuts = [round(steps * j / BATCHES) for j in range(BATCHES + 1)]
+    n_rep = steps // R
+    cuts = [round(n_rep * j / BATCHES) for j in range(BATCHES + 1)]
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(BATCHES + 1)]
     evs[0].record()
     i = 0
     for j in range(BATCHES):
         while i < cuts[j + 1]:
-            graphs[i % R].replay()
+            g_all.replay()
             i += 1
+        if j == BATCHES - 1 and g_rem is not None:
+            g_rem.replay()
         evs[j + 1].record()
     torch.cuda.synchronize()
     total_ms = evs[0].elapsed_time(evs[-1])
-    batch_ms = [evs[j].elapsed_time(evs[j + 1]) / (cuts[j + 1] - cuts[j]) for j in range(BATCHES) if cuts[j + 1] > cuts[j]]
+    batch_ms = [evs[j].elapsed_time(evs[j + 1]) / ((cuts[j + 1] - cuts[j]) * R) for j in range(BATCHES - 1)
+                if cuts[j + 1] > cuts[j]]
+    if not batch_ms:
+        batch_ms = [total_ms / steps]
+    one_ms = timed_batches(lambda i: g_one[i % R].replay(), 20 * R)
 
     n_kern = 200
     if fused:
@@ -416,11 +438,12 @@ def measure_step(cfg_name: str, steps: int, warmup: int, hwm=False, keys="bf16",
     res = {
         "inp": inp, "cfg": cfg, "R": R, "valid": valid, "T": T, "alg": alg,
         "ms_per_step": total_ms / steps, "step_us_median_of_batches": _median(batch_ms) * 1e3,
+        "one_step_graph_us": one_ms * 1e3,
         "score_us": score_avg_ms * 1e3, "topk_us": topk_avg_ms * 1e3,
         "k_GBs": alg["k"] / (score_avg_ms * 1e-3) / 1e9,
         "all_GBs": alg["total"] / (score_avg_ms * 1e-3) / 1e9,
     }
-    del sets, graphs, base
+    del sets, g_all, g_rem, g_one, base
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
     return res
@@ -432,6 +455,7 @@ def summary(r: dict) -> dict:
         "workload": f"{r['cfg'].name}: {r['cfg'].description}",
         "us_per_step": round(r["ms_per_step"] * 1e3, 2),
         "step_us_median_of_batches": round(r["step_us_median_of_batches"], 2),
+        "one_step_graph_us": round(r["one_step_graph_us"], 2),
         "valid_positions": r["valid"],
         "valid_positions_per_s": r["valid"] / (r["ms_per_step"] * 1e-3),
         "score_us": round(r["score_us"], 2), "topk_us": round(r["topk_us"], 2),
@@ -514,6 +538,7 @@ def main():
         "ms_per_step": head["ms_per_step"],
         "us_per_step": head["ms_per_step"] * 1e3,
         "step_us_median_of_batches": round(head["step_us_median_of_batches"], 3),
+        "one_step_graph_us": round(head["one_step_graph_us"], 3),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -525,7 +550,10 @@ def main():
             "max_pages": inp.max_pages, "max_c4": inp.max_c4, "valid_positions": head["valid"],
             "valid_pages": int(wl.pages_needed(inp.seq_lens).sum()), "topk": inp.topk, "seed": cfg.seed,
             "tail": "incremental (row_hwm)" if args.hwm else "stateless full -inf",
-            "input_copies": head["R"], "timing": f"hipGraph replay of [score; top-k], HIP events, {BATCHES} batches",
+            "input_copies": head["R"],
+            "timing": f"hipGraph replays of {head['R']} consecutive steps [score; top-k], one per input copy; "
+                      f"HIP events, {BATCHES} batches; one_step_graph_us: graphs of one step each, whose replay "
+                      f"adds a fixed launch cost per step",
             "accumulate": "fp32",
             "keys": "e4m3fn codes + float32 scale per key" if inp.fp8 else "bf16",
             "query_tokens": T,
