@@ -214,8 +214,8 @@ size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k
  *   stream     HIP stream to enqueue on
  *
  * Two kernels are enqueued. For rows longer than 4096 positions, a segment
- * kernel splits the row into segments of 4096 positions (up to 32 workgroups
- * per request, each taking every 32nd segment from its own), and writes each
+ * kernel splits the row into segments of 4096 positions (up to 8 workgroups
+ * per request, each taking every 8th segment from its own), and writes each
  * segment's likely members of the top k (keys at or above a
  * sampled cut, with their positions) to the workspace; a row kernel then
  * selects the top k of each row from those candidates, and falls back to a

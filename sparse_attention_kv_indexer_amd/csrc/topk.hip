@@ -18,8 +18,8 @@
 //
 // Two kernels, so that no workgroup ever waits on another one:
 //  * Segment kernel (rows longer than kSeg positions only; grid: requests x
-//    at most kSegGridY, 256 lanes, each workgroup taking every kSegGridY-th
-//    segment). A row is cut into segments of kSeg positions, so a
+//    at most kSegGridY (8), 256 lanes, each workgroup taking every
+//    kSegGridY-th segment). A row is cut into segments of kSeg positions, so a
 //    long row is read by many compute units at once; lane t of a segment's
 //    workgroup holds the 16 consecutive positions at 16 t in registers. Two
 //    sampled keys per lane are counted into a histogram of the first digit,
@@ -63,10 +63,11 @@ constexpr int kSeg = 4096;                    // positions per segment workgroup
 constexpr int kPerLane = kSeg / kSegThreads;  // 16 consecutive positions per lane
 constexpr int kSub = kSeg / kSegWaves;        // 1024 positions per wave: one sub-slot
 // Segment workgroups per request: each takes segments y, y + kSegGridY, ...
-// (rows of up to 32 segments, 128K tokens, get one workgroup per segment; a
-// wider row width no longer launches thousands of workgroups that only read a
-// short length and exit).
-constexpr int kSegGridY = 32;
+// Rows of up to 8 segments (a 128K-token row width) get one workgroup per
+// segment; a wider row width launches no more workgroups that only read a
+// short length and exit (measured at a 1M-token width with 512-token lengths:
+// cap 32 -> 8, top-k 7.24 -> 7.02 us; cap 4 makes 128K rows 2.4 us slower).
+constexpr int kSegGridY = 8;
 constexpr int kRecWords = 8;                  // per segment: kept count of each wave, cut key, unused
 
 constexpr int kRowThreads = 1024;             // row kernel
