@@ -105,6 +105,29 @@ def test_workload_parity(lib, name):
     say(f"attention {name}: worst error / bound {worst:.3f}")
 
 
+@pytest.mark.parametrize("name", ["c3", "full"])
+def test_on_the_gpu_top_k_selection(lib, name):
+    """The step as it runs: score and top-k on the GPU, then attention over the
+    top-k's own out_idx (ascending positions, -1 padding), checked against the
+    oracle's attention over that same selection; the selection itself is
+    checked against the oracle's top-k of the GPU's scores first."""
+    import torch
+
+    from gpu_helpers import check_topk_exact, run_score, run_topk
+
+    inp = wl.generate(name)
+    att = wl.attention_inputs(inp, 0)
+    say(f"attention on the GPU top-k of {name}")
+    got, t, out = run_score(lib, inp)
+    idx, vals = run_topk(lib, out, t["seq_lens"], inp.topk)
+    check_topk_exact(idx, vals, got, inp.seq_lens, inp.topk)
+    del t, out
+    torch.cuda.empty_cache()
+    o, l = run_attention(lib, inp.page_table, att, idx, wl.ATT_SCALE)
+    worst = check_attention(o, l, inp.page_table, att, idx, wl.ATT_SCALE)
+    say(f"attention on the GPU top-k of {name}: worst error / bound {worst:.3f}")
+
+
 def test_one_split_per_request(lib):
     """600 requests: one split each, written without the merge; ragged last tile (k = 100)."""
     inp = wl.random_case(11, 600, 3)

@@ -33,7 +33,8 @@ def check_mtp(got, inp, mt, page_table=None):
     return check_scores(got.reshape(B * T, N), ref.reshape(B * T, N), M.reshape(B * T, N), A.reshape(B * T, N))
 
 
-@pytest.mark.parametrize("name,tokens", [("tiny", 2), ("c2", 2), ("c2", 4), ("c3", 3), ("c3", 4)])
+@pytest.mark.parametrize("name,tokens", [("tiny", 2), ("c2", 2), ("c2", 4), ("c3", 3), ("c3", 4), ("full", 2),
+                                         ("stress1m", 3)])
 def test_workload_parity(lib, name, tokens):
     inp = wl.generate(name)
     mt = wl.mtp_inputs(inp, tokens, 0)
