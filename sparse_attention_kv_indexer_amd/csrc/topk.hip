@@ -441,9 +441,58 @@ __device__ __forceinline__ void clear_hists() {
   }
 }
 
+// The row kernel's pick over a histogram of kNB bins in LDS (complete, after
+// a barrier), shared by all its waves: lane t holds the kNB / 1024 bins just
+// below the top kNB / 1024 * t, each wave scans its lanes' counts, the wave
+// totals go through LDS, and the one lane whose bins hold the rank-th largest
+// counted key writes rs.bcast = {bin, keys in higher bins, keys in the bin}
+// ({0, total, 0} if rank exceeds the total). Every lane must call it; it ends
+// with a barrier, after which rs.bcast is read. (Wave 0 alone reading all
+// bins took about 0.75 us per pass.)
+template <int kNB>
+__device__ __forceinline__ void block_pick(const uint32_t* h, uint32_t rank) {
+  constexpr int kPer = kNB / kRowThreads;
+  static_assert(kPer == 1 || kPer == 2, "one or two bins per lane");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint32_t hi = (uint32_t)(kNB - 1 - kPer * tid);  // this lane's higher bin
+  uint32_t c_hi, c_lo = 0u;
+  if constexpr (kPer == 2) {
+    // bins hi - 1 (even) and hi share a 4-bin chunk, which hslot keeps in order
+    const u32x2 v = *reinterpret_cast<const u32x2*>(h + hslot(hi - 1));
+    c_lo = v.x;
+    c_hi = v.y;
+  } else {
+    c_hi = h[hslot(hi)];
+  }
+  const uint32_t c = c_hi + c_lo;
+  const uint32_t incl = wave_inclusive_scan(c);
+  if (lane == 63) rs.part[wave] = incl;
+  __syncthreads();
+  uint32_t pre = 0u, total = 0u;
+#pragma unroll
+  for (int w = 0; w < kRowWaves; ++w) {
+    const uint32_t t = rs.part[w];
+    pre += w < wave ? t : 0u;
+    total += t;
+  }
+  const uint32_t excl = pre + incl - c;
+  if (excl < rank && rank <= excl + c) {  // exactly one lane
+    const bool upper = rank <= excl + c_hi;
+    rs.bcast[0] = upper ? hi : hi - 1u;
+    rs.bcast[1] = upper ? excl : excl + c_hi;
+    rs.bcast[2] = upper ? c_hi : c_lo;
+  }
+  if (tid == 0 && rank > total) {
+    rs.bcast[0] = 0u;
+    rs.bcast[1] = total;
+    rs.bcast[2] = 0u;
+  }
+  __syncthreads();
+}
+
 // Resolves one digit: counts the keys matching (T, mask) into pass's
-// histogram with `count`; wave 0 picks the digit of the k-th largest and
-// hands it to the others through LDS.
+// histogram with `count`; the workgroup picks the digit of the k-th largest
+// (block_pick), which every lane then reads from LDS.
 // Returns how many keys match the resolved digits (the count in the chosen bin).
 template <int kPass, typename Count>
 __device__ __forceinline__ uint32_t radix_pass(uint32_t& T, uint32_t& mask, uint32_t& remaining, Count count) {
@@ -452,15 +501,7 @@ __device__ __forceinline__ uint32_t radix_pass(uint32_t& T, uint32_t& mask, uint
   uint32_t* h = pass_hist(kPass);
   count(h, shift, dmask);
   __syncthreads();
-  if ((threadIdx.x >> 6) == 0) {
-    const Pick p = wave_pick_lds<(kPass == 2 ? kBins / 2 : kBins)>(h, [&](uint32_t) { return remaining; });
-    if (threadIdx.x == 0) {
-      rs.bcast[0] = p.bin;
-      rs.bcast[1] = p.above;
-      rs.bcast[2] = h[hslot(p.bin)];
-    }
-  }
-  __syncthreads();
+  block_pick<(kPass == 2 ? kBins / 2 : kBins)>(h, remaining);
   // (bcast is written again only after the next pass's first barrier)
   T |= rs.bcast[0] << shift;
   remaining -= rs.bcast[1];
@@ -601,16 +642,8 @@ __device__ __noinline__ Kth select_candidates_ranged(int n, int k, uint32_t base
       if (kk >= base && (uint32_t)((uint64_t)o >> top) == prefix) atomicAdd(&h[hslot((o >> low) & dmask)], 1u);
     }
     __syncthreads();
-    if ((tid >> 6) == 0) {
-      const Pick p = pass < 2 ? wave_pick_lds<kBins>(h, [&](uint32_t) { return remaining; })
-                              : wave_pick_lds<kBins / 2>(h, [&](uint32_t) { return remaining; });
-      if (tid == 0) {
-        rs.bcast[0] = p.bin;
-        rs.bcast[1] = p.above;
-        rs.bcast[2] = h[hslot(p.bin)];
-      }
-    }
-    __syncthreads();
+    if (pass < 2) block_pick<kBins>(h, remaining);
+    else block_pick<kBins / 2>(h, remaining);
     prefix = (prefix << width) | rs.bcast[0];
     remaining -= rs.bcast[1];
     top = low;
