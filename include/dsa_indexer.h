@@ -185,7 +185,7 @@ int dsa_indexer_score_mtp(const void *q, const float *w, const void *k_pool, int
                           int32_t max_pages, float *logits, hipStream_t stream);
 
 /* Bytes of device workspace dsa_indexer_topk needs for these sizes: 0 when
- * max_c4 <= 4096 (the workspace may then be NULL) or the sizes are out of
+ * max_c4 <= 32768 (the workspace may then be NULL) or the sizes are out of
  * range, else batch * ceil(max_c4 / 4096) * (32 + 32768) bytes, about twice the
  * logits' own size. */
 size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k);
@@ -213,14 +213,17 @@ size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k
  *              their own
  *   stream     HIP stream to enqueue on
  *
- * Two kernels are enqueued. For rows longer than 4096 positions, a segment
- * kernel splits the row into segments of 4096 positions (up to 8 workgroups
- * per request, each taking every 8th segment from its own), and writes each
- * segment's likely members of the top k (keys at or above a
- * sampled cut, with their positions) to the workspace; a row kernel then
- * selects the top k of each row from those candidates, and falls back to a
- * select over the whole row whenever the candidates cannot be shown to hold
- * the whole top k. The result never depends on the sampling.
+ * One workgroup per request selects its row's top k. With max_c4 <= 32768 it
+ * is the only kernel: a row longer than 4096 positions is held in registers,
+ * cut at a sampled key (every 16th position), and the keys at or above the
+ * cut become the candidates. With a wider row width, a segment kernel is
+ * enqueued first: it splits each row longer than 4096 positions into
+ * segments of 4096 (up to 8 workgroups per request, each taking every 8th
+ * segment from its own) and writes each segment's keys at or above a cut
+ * sampled from that segment, with their positions, to the workspace, which
+ * the row's workgroup then gathers. Either way the row's workgroup falls back
+ * to a select over the whole row whenever the candidates cannot be shown to
+ * hold the whole top k, so the result never depends on the sampling.
  */
 int dsa_indexer_topk(const float *logits, const int32_t *seq_lens, int32_t batch, int32_t max_c4,
                      int32_t k, int32_t *out_idx, float *out_vals, void *workspace,
@@ -237,7 +240,8 @@ int dsa_indexer_topk(const float *logits, const int32_t *seq_lens, int32_t batch
  *   - Sizes whose dsa_indexer_topk_workspace_bytes(batch, max_c4, k) exceeds
  *     DSA_INDEXER_NOALLOC_SCRATCH_BYTES are refused with DSA_ERR_SCRATCH
  *     (64 MiB: batch * ceil(max_c4 / 4096) up to 2046, e.g. 64 requests of a
- *     128K-token row width; rows of at most 4096 positions need none).
+ *     row width up to 126976 positions; a row width of at most 32768
+ *     positions needs none).
  *   - The first call on a device that needs the array resolves its address
  *     there (hipGetSymbolAddress, no allocation); make that first call
  *     outside graph capture.
@@ -262,7 +266,7 @@ int dsa_indexer_topk_noalloc(const float *logits, const int32_t *seq_lens, int32
  *
  * The histogram gives every row's first radix digit of the k-th largest
  * score exactly, so no cut is sampled and the first radix pass is skipped:
- * each segment keeps the keys in or above that bin. Counts that do not
+ * the candidates are the keys in or above that bin. Counts that do not
  * belong to these logits give unspecified positions (never accesses outside
  * the buffers). Errors as for dsa_indexer_topk (DSA_ERR_NULL also for a NULL
  * hist, DSA_ERR_ALIGN for a misaligned one); the workspace is sized by

@@ -1,7 +1,8 @@
 // Top-k for callers that cannot allocate device memory: code under hipGraph
 // capture, tight serving loops, harnesses that forbid hipMalloc. The same
-// segment and row kernels as dsa_indexer_topk, with their workspace in a
-// fixed device array instead of a caller buffer.
+// kernels as dsa_indexer_topk, with their workspace (needed only for a row
+// width above 32768 positions) in a fixed device array instead of a caller
+// buffer.
 //
 // The array is a file-scope __device__ variable: each GPU the library runs on
 // holds its own copy, at its own address, from module load until the process

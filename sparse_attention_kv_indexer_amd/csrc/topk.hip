@@ -72,13 +72,26 @@ constexpr int kRecWords = 8;                  // per segment: kept count of each
 
 constexpr int kRowThreads = 1024;             // row kernel
 constexpr int kRowWaves = kRowThreads / 64;
-constexpr int kCap = 16384;                   // candidates a row workgroup holds in LDS
+// LDS words of cand_key and of cand_pos each: 16380 keeps the distance
+// between cand_key[i] and cand_pos[i] within an LDS instruction's 16-bit
+// offset, so one address serves both stores.
+constexpr int kSlots = 16380;
+constexpr int kCap = kSlots - kRowThreads;    // candidates a row workgroup holds in LDS (then one spare slot per lane)
 constexpr int kRound = 256;                   // sub-slot records per gather round
 constexpr int kSpecSlots = 32;                // sub-slots read before their counts are known
 constexpr int kSpec = 256;                    // pairs read ahead per such sub-slot
 constexpr int kSweep = 16 * kRowThreads;      // positions per block of the whole-row output sweep
 constexpr int kSmall = 64;                    // keys of a bin that one wave ranks directly
 constexpr int kSmallRanged = 16;              // the same, in the ranged select over long rows' candidates
+// A row width of at most kRes positions needs no segment kernel: the row
+// kernel holds a whole row in registers (kResBlk blocks of kSeg positions,
+// four consecutive positions of each per lane) and cuts it itself, from
+// every kSampleStride-th position.
+constexpr int kRes = 32768;
+constexpr int kResBlk = kRes / kSeg;
+constexpr int kSampleStride = 16;             // the sample: every 16th position
+static_assert(kSeg == 4 * kRowThreads, "a block of kSeg positions is one 16-byte group per lane");
+static_assert(2 * kBins <= kCap, "the sample histograms fit in cand_pos");
 
 static_assert(kSegWaves * 64 == kSegThreads && kPerLane * kSegThreads == kSeg, "segment work split");
 static_assert(2 * kRowThreads * 4 == kSpecSlots * kSpec, "read-ahead: four 16-byte loads per lane");
@@ -404,15 +417,17 @@ __global__ __launch_bounds__(kSegThreads) void topk_segment_kernel(const float* 
 // LDS of the row kernel, at namespace scope so the out-of-line whole-row path
 // reaches it with LDS instructions too.
 struct RowShared {
+  // first, so that cand_pos[i] is cand_key[i]'s address plus an offset that
+  // an LDS instruction holds
+  __attribute__((aligned(16))) uint32_t cand_key[kSlots];
+  __attribute__((aligned(16))) uint32_t cand_pos[kSlots];
   __attribute__((aligned(16))) uint32_t hist0[kBins];  // one histogram per radix pass
   __attribute__((aligned(16))) uint32_t hist1[kBins];
   __attribute__((aligned(16))) uint32_t hist2[kBins / 2];
-  uint32_t cand_key[kCap];
-  uint32_t cand_pos[kCap];
   uint32_t cnt[kRound];   // per sub-slot of a gather round: kept count
   uint32_t off[kRound];   //   its first candidate
   uint32_t roff[kRound];  //   its first pair not read ahead, in the round's list of those
-  uint32_t part[2 * kRowWaves];
+  uint32_t part[4 * kRowWaves];
   uint32_t bcast[3];
   uint32_t hpick[3];  // from the score kernel's histogram: bin of the k-th largest, count above it, found
   uint32_t small[kSmall];  // the keys of the last bin, once at most kSmall remain
@@ -445,12 +460,12 @@ __device__ __forceinline__ void clear_hists() {
 // a barrier), shared by all its waves: lane t holds the kNB / 1024 bins just
 // below the top kNB / 1024 * t, each wave scans its lanes' counts, the wave
 // totals go through LDS, and the one lane whose bins hold the rank-th largest
-// counted key writes rs.bcast = {bin, keys in higher bins, keys in the bin}
-// ({0, total, 0} if rank exceeds the total). Every lane must call it; it ends
-// with a barrier, after which rs.bcast is read. (Wave 0 alone reading all
-// bins took about 0.75 us per pass.)
-template <int kNB>
-__device__ __forceinline__ void block_pick(const uint32_t* h, uint32_t rank) {
+// counted key (rank = rank_of(total counted)) writes rs.bcast = {bin, keys in
+// higher bins, keys in the bin} ({0, total, 0} if rank exceeds the total).
+// Every lane must call it; it ends with a barrier, after which rs.bcast is
+// read. (Wave 0 alone reading all bins took about 0.75 us per pass.)
+template <int kNB, typename RankOf>
+__device__ __forceinline__ void block_pick(const uint32_t* h, RankOf rank_of) {
   constexpr int kPer = kNB / kRowThreads;
   static_assert(kPer == 1 || kPer == 2, "one or two bins per lane");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -475,6 +490,7 @@ __device__ __forceinline__ void block_pick(const uint32_t* h, uint32_t rank) {
     pre += w < wave ? t : 0u;
     total += t;
   }
+  const uint32_t rank = rank_of(total);
   const uint32_t excl = pre + incl - c;
   if (excl < rank && rank <= excl + c) {  // exactly one lane
     const bool upper = rank <= excl + c_hi;
@@ -501,7 +517,7 @@ __device__ __forceinline__ uint32_t radix_pass(uint32_t& T, uint32_t& mask, uint
   uint32_t* h = pass_hist(kPass);
   count(h, shift, dmask);
   __syncthreads();
-  block_pick<(kPass == 2 ? kBins / 2 : kBins)>(h, remaining);
+  block_pick<(kPass == 2 ? kBins / 2 : kBins)>(h, [&](uint32_t) { return remaining; });
   // (bcast is written again only after the next pass's first barrier)
   T |= rs.bcast[0] << shift;
   remaining -= rs.bcast[1];
@@ -601,23 +617,26 @@ __device__ __forceinline__ Kth select_candidates(int n, int k, bool from_hist, u
 // digit, where the first pass would pile its LDS atomics onto a few words).
 // Returns r = 0xFFFFFFFF if fewer than k keys reach base (T < base: the caller
 // selects over the whole row). Out of line, like the whole-row path, so that
-// the common path's code stays as it is. The histograms are clear and
-// rs.range is (0, 0) on entry.
-__device__ __noinline__ Kth select_candidates_ranged(int n, int k, uint32_t base) {
+// the common path's code stays as it is. The histograms are clear on entry,
+// and rs.range is (0, 0), or with preset the count of candidates at or above
+// base and the largest key.
+__device__ __noinline__ Kth select_candidates_ranged(int n, int k, uint32_t base, bool preset) {
   const int tid = threadIdx.x;
-  uint32_t hi = 0u, above = 0u;
-  for (int i = tid; i < n; i += kRowThreads) {
-    const uint32_t kk = rs.cand_key[i];
-    hi = max(hi, kk);
-    above += kk >= base ? 1u : 0u;
+  if (!preset) {  // (else the gather left rs.range set)
+    uint32_t hi = 0u, above = 0u;
+    for (int i = tid; i < n; i += kRowThreads) {
+      const uint32_t kk = rs.cand_key[i];
+      hi = max(hi, kk);
+      above += kk >= base ? 1u : 0u;
+    }
+    hi = wave_max(hi);
+    above = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(above), 63);
+    if ((tid & 63) == 0) {
+      atomicAdd(&rs.range[0], above);
+      atomicMax(&rs.range[1], hi);
+    }
+    __syncthreads();
   }
-  hi = wave_max(hi);
-  above = (uint32_t)__builtin_amdgcn_readlane((int)wave_inclusive_scan(above), 63);
-  if ((tid & 63) == 0) {
-    atomicAdd(&rs.range[0], above);
-    atomicMax(&rs.range[1], hi);
-  }
-  __syncthreads();
   if (rs.range[0] < (uint32_t)k) return Kth{0u, 0xFFFFFFFFu};
   const uint32_t span = rs.range[1] - base;
   int top = span == 0u ? 0 : 32 - __builtin_clz(span);  // bits of the offsets still to resolve
@@ -642,8 +661,8 @@ __device__ __noinline__ Kth select_candidates_ranged(int n, int k, uint32_t base
       if (kk >= base && (uint32_t)((uint64_t)o >> top) == prefix) atomicAdd(&h[hslot((o >> low) & dmask)], 1u);
     }
     __syncthreads();
-    if (pass < 2) block_pick<kBins>(h, remaining);
-    else block_pick<kBins / 2>(h, remaining);
+    if (pass < 2) block_pick<kBins>(h, [&](uint32_t) { return remaining; });
+    else block_pick<kBins / 2>(h, [&](uint32_t) { return remaining; });
     prefix = (prefix << width) | rs.bcast[0];
     remaining -= rs.bcast[1];
     top = low;
@@ -842,6 +861,182 @@ __device__ __forceinline__ int gather_segments(const uint32_t* __restrict__ ws, 
   return n;
 }
 
+// Inclusive scans of the kN values of every lane over the workgroup's lanes in
+// lane order, and their totals. Every lane must call it; it ends with a
+// barrier, after which rs.part may be rewritten.
+template <int kN>
+__device__ __forceinline__ void block_scan_n(uint32_t (&v)[kN], uint32_t (&tot)[kN]) {
+  static_assert(kN * kRowWaves <= 4 * kRowWaves, "rs.part holds four values per wave");
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int q = 0; q < kN; ++q) v[q] = wave_inclusive_scan(v[q]);
+  if (lane == 63) {
+#pragma unroll
+    for (int q = 0; q < kN; ++q) rs.part[q * kRowWaves + wave] = v[q];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int q = 0; q < kN; ++q) {
+    uint32_t add = 0u, all = 0u;
+#pragma unroll
+    for (int w = 0; w < kRowWaves; ++w) {
+      const uint32_t p = rs.part[q * kRowWaves + w];
+      add += w < wave ? p : 0u;
+      all += p;
+    }
+    v[q] += add;
+    tot[q] = all;
+  }
+  __syncthreads();
+}
+
+// The candidates of a row of kSeg < len <= kRes positions when the row width
+// is at most kRes (no segment kernel ran): the workgroup loads the whole row
+// into registers (lane t: positions 4t .. 4t + 3 of every block of kSeg), cuts
+// it, and writes the keys at or above the cut with their positions to LDS in
+// position order. Returns the candidate count, or -1 if more than kCap. Sets
+// rs.max_cut to the cut, which the select and its check then treat as the
+// largest segment cut: if the k-th largest key lies below it, the row takes
+// the whole-row select, so the cut never changes the result. Also sets
+// rs.range to (the count, the largest candidate key), which the ranged
+// select would otherwise sweep the candidates for.
+//
+// The cut: with the score kernel's histogram (hint, and wave 0's pick of it
+// in rs.hpick), that pick's bin edge. Otherwise the sample of every
+// kSampleStride-th position (n_s keys, held by every fourth lane) is counted
+// into a first-digit histogram, and the cut is the lower edge of the bin
+// holding its rank_s-th largest, rank_s = 1.1 m + 4 sqrt(m) + 4 for m = k n_s
+// / len the sample's expected share of the top k; a bin holding more than 32
+// samples is split by a second digit over the samples in it. (On the c3
+// workload's rows longer than 4096: about 3000 candidates for k = 2048.) The
+// sample histograms live in rs.cand_pos, which the candidates overwrite
+// afterwards. The three radix histograms are untouched.
+//
+// Writing the candidates: every lane stores every key it holds, a kept one at
+// its place in position order and any other one in the lane's spare slot
+// past kCap, so the stores need no branch; the keys are stored as the raw
+// score bits and turned into keys afterwards, over the candidates only.
+__device__ __forceinline__ int gather_resident(const float* row_ptr, int len, int k, bool hint) {
+  const int tid = threadIdx.x;
+  const int n_blk = (len + kSeg - 1) / kSeg;  // 2 .. kResBlk
+  // only positions [0, len) are readable through r1: a 16-byte load reaching
+  // past len reads 0 for each word past it (the range is checked per word)
+  const rsrc_t r1 = make_rsrc(row_ptr, (uint32_t)len * 4u);
+  u32x4 v[kResBlk];
+#pragma unroll
+  for (int j = 0; j < kResBlk; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(r1, (j * kSeg + 4 * tid) * 4, 0, 0);
+  const u32x4 zero4 = {0u, 0u, 0u, 0u};
+  uint32_t* sample_hist = rs.cand_pos;  // two histograms of kBins
+  *reinterpret_cast<u32x4*>(sample_hist + 4 * tid) = zero4;
+  static_assert(4 * kRowThreads == 2 * kBins, "one 16-byte store per lane clears both");
+  __syncthreads();
+
+  uint32_t lo;
+  const uint32_t n_s = (uint32_t)(len + kSampleStride - 1) / kSampleStride;
+  const float m = (float)k * (float)n_s / (float)len;
+  const float want = 1.1f * m + 4.0f * sqrtf(m) + 4.0f;
+  if (hint && rs.hpick[2] != 0u) {
+    lo = max(rs.hpick[0] << 21, 1u);
+  } else if (want >= (float)n_s) {
+    lo = 1u;  // every valid key
+  } else {
+    const uint32_t rank_s = (uint32_t)want;  // 1 .. n_s - 1
+    // this lane's sampled keys (lanes 4i: position 16i of every block), 0 if none
+    constexpr int kPerBlk = kSeg / kSampleStride / (kRowThreads / 4);
+    static_assert(kPerBlk == 1, "one sampled position per block in every fourth lane");
+    uint32_t sk[kResBlk];
+#pragma unroll
+    for (int j = 0; j < kResBlk; ++j) {
+      const bool in = (tid & 3) == 0 && j * kSeg + 4 * tid < len;
+      sk[j] = in ? order_key(__uint_as_float(v[j][0])) : 0u;
+    }
+    if ((tid & 3) == 0) {
+#pragma unroll
+      for (int j = 0; j < kResBlk; ++j)
+        if (sk[j] != 0u) atomicAdd(&sample_hist[hslot(sk[j] >> 21)], 1u);
+    }
+    __syncthreads();
+    block_pick<kBins>(sample_hist, [&](uint32_t) { return rank_s; });  // the total is n_s
+    const uint32_t b0 = rs.bcast[0], above = rs.bcast[1], in_bin = rs.bcast[2];
+    lo = b0 << 21;
+    if (in_bin > 32u) {
+      uint32_t* h2 = sample_hist + kBins;
+      if ((tid & 3) == 0) {
+#pragma unroll
+        for (int j = 0; j < kResBlk; ++j)
+          if (sk[j] != 0u && (sk[j] >> 21) == b0) atomicAdd(&h2[hslot((sk[j] >> 10) & 0x7FFu)], 1u);
+      }
+      __syncthreads();
+      block_pick<kBins>(h2, [&](uint32_t) { return rank_s - above; });
+      lo |= rs.bcast[0] << 10;
+    }
+    lo = max(lo, 1u);
+  }
+
+  // key >= lo <=> score >= the float of lo, except that NaN (key 1) passes
+  // only when lo is at or below -inf's key: then every valid key is kept
+  const bool keep_all = lo <= 0x007FFFFFu;
+  const float f = __uint_as_float(key_to_bits(lo));
+  auto kept = [&](int j, int e) -> bool {
+    return (keep_all || __uint_as_float(v[j][e]) >= f) && j * kSeg + 4 * tid + e < len;
+  };
+  uint32_t pk[kResBlk / 2];  // kept counts of blocks 2q and 2q + 1, 16 bits each
+#pragma unroll
+  for (int q = 0; q < kResBlk / 2; ++q) {
+    uint32_t c0 = 0u, c1 = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      c0 += kept(2 * q, e) ? 1u : 0u;
+      c1 += kept(2 * q + 1, e) ? 1u : 0u;
+    }
+    pk[q] = c0 | (c1 << 16);
+  }
+  uint32_t incl[kResBlk / 2], tot[kResBlk / 2];
+#pragma unroll
+  for (int q = 0; q < kResBlk / 2; ++q) incl[q] = pk[q];
+  block_scan_n<kResBlk / 2>(incl, tot);  // 16-bit fields: at most kSeg per block
+  uint32_t n = 0u, off[kResBlk];
+#pragma unroll
+  for (int j = 0; j < kResBlk; ++j) {
+    const int sh = 16 * (j & 1);
+    off[j] = n + ((incl[j / 2] >> sh) & 0xFFFFu) - ((pk[j / 2] >> sh) & 0xFFFFu);
+    n += (tot[j / 2] >> sh) & 0xFFFFu;
+  }
+  if (n > (uint32_t)kCap) return -1;  // workgroup-uniform
+  // byte offsets into rs.cand_key (rs.cand_pos lies kSlots words further)
+  const uint32_t spare = 4u * (uint32_t)(kCap + tid);
+  char* const ck = reinterpret_cast<char*>(rs.cand_key);
+#pragma unroll
+  for (int j = 0; j < kResBlk; ++j) {
+    if (j < n_blk) {
+      uint32_t o = 4u * off[j];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const bool c = kept(j, e);
+        uint32_t* at = reinterpret_cast<uint32_t*>(ck + (c ? o : spare));
+        at[0] = v[j][e];
+        at[kSlots] = (uint32_t)(j * kSeg + 4 * tid + e);  // rs.cand_pos
+        o += c ? 4u : 0u;
+      }
+    }
+  }
+  __syncthreads();
+  // the candidates' keys, and the largest of them
+  uint32_t mx = 0u;
+  for (int i = tid; i < (int)n; i += kRowThreads) {
+    const uint32_t kk = order_key(__uint_as_float(rs.cand_key[i]));
+    rs.cand_key[i] = kk;
+    mx = max(mx, kk);
+  }
+  mx = wave_max(mx);
+  if ((tid & 63) == 0) atomicMax(&rs.range[1], mx);
+  if (tid == 0) {
+    rs.range[0] = n;
+    rs.max_cut = lo;
+  }
+  return (int)n;
+}
+
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ logits,
                                                                 const int32_t* __restrict__ seq_lens,
                                                                 int32_t max_c4, int32_t k,
@@ -898,6 +1093,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
       }
     }
     n = len;
+  } else if (max_c4 <= kRes) {
+    n = gather_resident(row_ptr, len, k, hist != nullptr);
   } else {
     n = gather_segments(ws, b, (int)gridDim.x, n_seg, len);
   }
@@ -927,7 +1124,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     // gathered candidates: the select over those at or above the largest cut
     // (with a histogram that the candidates did not confirm, the ranged select
     // over the candidates at or above the largest cut decides, as without one)
-    const Kth t = (!from_hist && len > kSeg) ? select_candidates_ranged(n, k, rs.max_cut)
+    const Kth t = (!from_hist && len > kSeg) ? select_candidates_ranged(n, k, rs.max_cut, max_c4 <= kRes)
                                              : select_candidates(n, k, from_hist, bin0, above0);
     // every key a segment left out lies below its cut, hence below T
     if (t.r != 0xFFFFFFFFu && t.T >= rs.max_cut) {
@@ -944,7 +1141,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
 }  // namespace
 
 size_t topk_workspace_words(int32_t batch, int32_t max_c4) {
-  if (max_c4 <= kSeg) return 0;  // no row can need the segment kernel
+  if (max_c4 <= kRes) return 0;  // no segment kernel
   const size_t n_seg = ((size_t)max_c4 + kSeg - 1) / kSeg;
   return (size_t)batch * n_seg * (kRecWords + 2 * kSeg);  // records, then pairs
 }
@@ -954,8 +1151,9 @@ hipError_t launch_topk(const float* logits, const int32_t* seq_lens, int32_t bat
                        hipStream_t stream) {
   const int n_seg = (int)(((int64_t)max_c4 + kSeg - 1) / kSeg);
   uint32_t* ws = static_cast<uint32_t*>(workspace);
-  // a row reaches the segment kernel only if it is longer than kSeg and than k
-  if (max_c4 > kSeg && k < max_c4)
+  // a row reaches the segment kernel only if it is longer than kSeg and than
+  // k, and only where the row width exceeds kRes
+  if (max_c4 > kRes && k < max_c4)
     hipLaunchKernelGGL(topk_segment_kernel, dim3(batch, min(n_seg, kSegGridY)), dim3(kSegThreads), 0, stream, logits, seq_lens,
                        max_c4, k, n_seg, ws, hist);
   hipLaunchKernelGGL(topk_row_kernel, dim3(batch), dim3(kRowThreads), 0, stream, logits, seq_lens, max_c4, k,

@@ -90,14 +90,16 @@ def test_topk_rejects(lib, over, want):
 
 
 def test_topk_workspace_contract(lib):
-    need = lib.dsa_indexer_topk_workspace_bytes(64, 32768, 2048)
-    assert need == 64 * 8 * (8 + 2 * 4096) * 4
-    assert lib.dsa_indexer_topk_workspace_bytes(64, 4096, 64) == 0  # one segment: no workspace
-    assert lib.dsa_indexer_topk_workspace_bytes(0, 32768, 2048) == 0
+    need = lib.dsa_indexer_topk_workspace_bytes(64, 65536, 2048)
+    assert need == 64 * 16 * (8 + 2 * 4096) * 4
+    assert lib.dsa_indexer_topk_workspace_bytes(64, 32769, 2048) == 64 * 9 * (8 + 2 * 4096) * 4
+    assert lib.dsa_indexer_topk_workspace_bytes(64, 32768, 2048) == 0  # rows held in registers: no workspace
+    assert lib.dsa_indexer_topk_workspace_bytes(64, 4096, 64) == 0
+    assert lib.dsa_indexer_topk_workspace_bytes(0, 65536, 2048) == 0
     # every call below fails validation (nothing may reach a launch in these host-only tests)
-    assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=32768, k=2048, workspace=A, ws_bytes=need - 1)) == WS
-    assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=32768, k=2048, workspace=None, ws_bytes=need)) == WS
-    assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=32768, k=2048, workspace=A + 4, ws_bytes=need)) == ALIGN
+    assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=65536, k=2048, workspace=A, ws_bytes=need - 1)) == WS
+    assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=65536, k=2048, workspace=None, ws_bytes=need)) == WS
+    assert lib.dsa_indexer_topk(*topk_args(batch=64, max_c4=65536, k=2048, workspace=A + 4, ws_bytes=need)) == ALIGN
 
 
 def score_hist_args(**over):
@@ -128,7 +130,7 @@ def topk_hist_args(**over):
 @pytest.mark.parametrize("over,want", [(dict(logits=None), NULL), (dict(hist=None), NULL), (dict(out_idx=None), NULL),
                                        (dict(batch=0), SHAPE), (dict(k=0), K), (dict(k=129), K),
                                        (dict(hist=A + 4), ALIGN), (dict(out_idx=A + 2), ALIGN),
-                                       (dict(batch=64, max_c4=32768, k=2048, ws_bytes=64 * 8 * (8 + 2 * 4096) * 4 - 1),
+                                       (dict(batch=64, max_c4=65536, k=2048, ws_bytes=64 * 16 * (8 + 2 * 4096) * 4 - 1),
                                         WS)])
 def test_topk_hist_rejects(lib, over, want):
     assert lib.dsa_indexer_topk_hist(*topk_hist_args(**over)) == want
@@ -250,7 +252,8 @@ def noalloc_args(**over):
                                        (dict(k=0), K), (dict(k=129), K), (dict(out_idx=A + 2), ALIGN),
                                        (dict(out_vals=A + 1), ALIGN), (dict(logits=A + 3), ALIGN),
                                        (dict(batch=64, max_c4=4096 * 32, k=64), SCRATCH),
-                                       (dict(batch=2048, max_c4=4097, k=64), SCRATCH)])
+                                       (dict(batch=2048, max_c4=32769, k=64), SCRATCH),
+                                       (dict(batch=228, max_c4=32769, k=64), SCRATCH)])
 def test_topk_noalloc_rejects(lib, over, want):
     """Host-side refusals of the allocation-free top-k, sizes past its fixed
     array included (64 MiB: at most 2046 segment slots of 4096 positions)."""
@@ -261,7 +264,9 @@ def test_topk_noalloc_limit_matches_the_header(lib):
     text = open(HEADER).read()
     assert "#define DSA_INDEXER_NOALLOC_SCRATCH_BYTES (64u << 20)" in text
     per_slot = 32 + 32768  # a segment's record, then its (key, position) pairs
-    assert "* (32 + 32768) bytes" in text and "up to 2046" in text
-    assert lib.dsa_indexer_topk_workspace_bytes(2046, 4097, 64) == 2046 * 2 * per_slot
-    assert lib.dsa_indexer_topk_workspace_bytes(2046, 4096, 64) == 0
+    assert "* (32 + 32768) bytes" in text and "up to 2046" in text and "up to 126976 positions" in text
+    assert lib.dsa_indexer_topk_workspace_bytes(186, 11 * 4096, 64) == 2046 * per_slot
+    assert lib.dsa_indexer_topk_workspace_bytes(64, 126976, 64) == 64 * 31 * per_slot <= (64 << 20)
+    assert lib.dsa_indexer_topk_workspace_bytes(64, 126977, 64) > (64 << 20)
+    assert lib.dsa_indexer_topk_workspace_bytes(65535, 32768, 64) == 0  # no segment kernel: none
     assert 2046 * per_slot <= (64 << 20) < 2047 * per_slot

@@ -49,17 +49,19 @@ def _replay_and_compare(lib, g, outs, expected, poison):
         run_score(lib, wl.generate("tiny"))  # eager work between replays
 
 
-def test_graph_long_rows_score_and_topk(lib):
-    """Rows of up to 10240 positions: three top-k segments per row, so the
-    segment kernel and the workspace are inside the graph."""
+@pytest.mark.parametrize("max_pages", [160, 640])
+def test_graph_long_rows_score_and_topk(lib, max_pages):
+    """Rows of up to 10240 positions, held in the top-k's registers (no
+    workspace), and of up to 40960, where the segment kernel and the
+    workspace are inside the graph."""
     import torch
 
-    inp = wl.random_case(31, 8, 160, topk=300)
-    say("graph long rows B=8 max_pages=160 k=300")
+    inp = wl.random_case(31, 8, max_pages, topk=300)
+    say(f"graph long rows B=8 max_pages={max_pages} k=300")
     t = lib.to_device(inp)
     B, N, k = inp.batch, inp.max_c4, inp.topk
     ws = lib.topk_workspace(B, N, k)
-    assert ws is not None
+    assert (ws is not None) == (N > 32768)
     out = torch.empty((B, N), dtype=torch.float32, device="cuda")
     idx = torch.empty((B, k), dtype=torch.int32, device="cuda")
     vals = torch.empty((B, k), dtype=torch.float32, device="cuda")

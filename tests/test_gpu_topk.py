@@ -29,6 +29,22 @@ def _upload(x, lens):
             torch.from_numpy(np.asarray(lens, dtype=np.int32)).cuda())
 
 
+# Row widths of at most 32768 positions keep each row in the row workgroup's
+# registers (one kernel); a wider row width sends rows longer than 4096
+# through the segment kernel. Tests of the cut and its fallbacks run both.
+SEGMENT_WIDTH = 40960
+
+
+def _widen(x, width):
+    """x in the first columns of a row width of `width`, NaN past them (never read)."""
+    B, N = x.shape
+    if width == N:
+        return x
+    out = np.full((B, width), np.nan, np.float32)
+    out[:, :N] = x
+    return out
+
+
 @pytest.mark.parametrize("k", [1, 5, 64, 1000, 1024, 1025, 4096])
 def test_random_rows(lib, k):
     rng = np.random.default_rng(k)
@@ -95,7 +111,8 @@ def test_without_values(lib):
     check_topk_exact(idx, None, x, lens, 100)
 
 
-def test_sampled_cut_fallbacks(lib):
+@pytest.mark.parametrize("width", [32768, SEGMENT_WIDTH])
+def test_sampled_cut_fallbacks(lib, width):
     """Rows longer than the candidate capacity whose sampled cut cannot be
     used: all keys equal (too many candidates), and large scores placed
     exactly where one key per 32 is sampled (too few keys above the cut)."""
@@ -109,8 +126,8 @@ def test_sampled_cut_fallbacks(lib):
     x[2] = np.round(rng.standard_normal(N) * 2).astype(np.float32)  # a handful of distinct values
     lens = np.array([20000, 32768, 30001])
     for k in (100, 2048, 5000):
-        say(f"topk sampled-cut fallbacks k={k}")
-        xd, ld = _upload(x, lens)
+        say(f"topk sampled-cut fallbacks k={k} width={width}")
+        xd, ld = _upload(_widen(x, width), lens)
         idx, vals = run_topk(lib, xd, ld, k)
         check_topk_exact(idx, vals, x, lens, k)
 
@@ -130,11 +147,12 @@ def test_rows_with_many_segments(lib):
         check_topk_exact(idx, vals, x, lens, k)
 
 
-def test_large_batch(lib):
+@pytest.mark.parametrize("N", [20000, SEGMENT_WIDTH])
+def test_large_batch(lib, N):
     """More than 64 requests with mixed lengths: rows of one segment, of many
     segments, shorter than k, and empty."""
     rng = np.random.default_rng(11)
-    B, N, k = 200, 20000, 300
+    B, k = 200, 300
     x = rng.standard_normal((B, N)).astype(np.float32)
     lens = rng.integers(0, N, size=B, endpoint=True)
     lens[::7] = 0
@@ -146,23 +164,26 @@ def test_large_batch(lib):
     check_topk_exact(idx, vals, x, lens, k)
 
 
-def test_segment_cut_above_kth_falls_back(lib):
+@pytest.mark.parametrize("width", [16384, SEGMENT_WIDTH])
+def test_segment_cut_above_kth_falls_back(lib, width):
     """One segment holds every large score, so its share of the top k is far
     above the average its cut aims at: its cut lies above the k-th largest key,
-    and the row kernel must select over the whole row instead."""
+    and the row kernel must select over the whole row instead (with the row
+    in registers the same rows check an ordinary cut)."""
     rng = np.random.default_rng(14)
     B, N, k = 2, 16384, 2048
     x = rng.standard_normal((B, N)).astype(np.float32)
     x[0, :4096] = 1000.0 + rng.random(4096).astype(np.float32)
     x[1, 8192:12288] = 50.0 + np.round(rng.random(4096) * 8).astype(np.float32)  # ties among the large ones
     lens = np.array([16384, 16000])
-    say("topk segment cut above the k-th key")
-    xd, ld = _upload(x, lens)
+    say(f"topk segment cut above the k-th key width={width}")
+    xd, ld = _upload(_widen(x, width), lens)
     idx, vals = run_topk(lib, xd, ld, k)
     check_topk_exact(idx, vals, x, lens, k)
 
 
-def test_too_few_candidates_falls_back(lib):
+@pytest.mark.parametrize("width", [32768, SEGMENT_WIDTH])
+def test_too_few_candidates_falls_back(lib, width):
     """Large scores exactly at the segment kernel's sampled slots (lane t of a
     4096-position segment samples offsets 16t + (t % 16) and
     16t + ((t + 8) % 16)) make every segment's cut keep little more than the
@@ -176,13 +197,14 @@ def test_too_few_candidates_falls_back(lib):
         for off in (16 * t + (t % 16), 16 * t + ((t + 8) % 16)):
             x[:, s0 + off] = 500.0 + rng.random(256).astype(np.float32)
     lens = np.array([32768, 30000])
-    say("topk too few candidates")
-    xd, ld = _upload(x, lens)
+    say(f"topk too few candidates width={width}")
+    xd, ld = _upload(_widen(x, width), lens)
     idx, vals = run_topk(lib, xd, ld, k)
     check_topk_exact(idx, vals, x, lens, k)
 
 
-def test_long_rows_with_narrow_candidate_ranges(lib):
+@pytest.mark.parametrize("width", [32768, SEGMENT_WIDTH])
+def test_long_rows_with_narrow_candidate_ranges(lib, width):
     """Rows longer than one segment select over the candidates at or above
     the largest segment cut, on digits of their offset from it: candidates
     that are all one value (no digit left to resolve), two values one ulp
@@ -200,7 +222,46 @@ def test_long_rows_with_narrow_candidate_ranges(lib):
     x[4] = rng.standard_normal(N).astype(np.float32) * np.float32(1e-3) + 7.0  # narrow range of all keys
     x[5, top] = rng.integers(0, 4, size=top.size).astype(np.float32) + 10.0  # ties among few top values
     lens = np.array([N, N, N, 24000, 30001, N])
-    say("topk long rows, narrow candidate ranges")
+    say(f"topk long rows, narrow candidate ranges width={width}")
+    xd, ld = _upload(_widen(x, width), lens)
+    idx, vals = run_topk(lib, xd, ld, k)
+    check_topk_exact(idx, vals, x, lens, k)
+
+
+@pytest.mark.parametrize("k", [100, 1000, 2048, 2100])
+def test_resident_sample_defeated(lib, k):
+    """Rows held in registers take their cut from every 16th position: large
+    scores at exactly those positions put the cut among them, so fewer than k
+    keys reach it whenever k exceeds the sample's rank target, and the row
+    must be selected over whole. Next to them, rows whose sampled positions
+    are the smallest keys (the cut keeps nearly every key), and an ordinary
+    row."""
+    rng = np.random.default_rng(21)
+    B, N = 4, 32768
+    x = rng.standard_normal((B, N)).astype(np.float32)
+    x[0, ::16] = 1000.0 + rng.random(N // 16).astype(np.float32)
+    x[1, ::16] = 1000.0  # and tied
+    x[2, ::16] = -1000.0 - rng.random(N // 16).astype(np.float32)
+    lens = np.array([32768, 30001, 29999, 17000])
+    say(f"topk resident sample defeated k={k}")
     xd, ld = _upload(x, lens)
+    idx, vals = run_topk(lib, xd, ld, k)
+    check_topk_exact(idx, vals, x, lens, k)
+
+
+@pytest.mark.parametrize("width", [4099, 32767])
+def test_odd_row_widths(lib, width):
+    """Row widths that are not a multiple of 4 (rows start at any 4-byte
+    boundary) with lengths ending anywhere in a 16-byte group: the 16-byte
+    loads of rows held in registers read only positions below the length."""
+    rng = np.random.default_rng(width)
+    B, k = 9, 1000
+    x = rng.standard_normal((B, width)).astype(np.float32)
+    lens = np.clip(np.array([width, width - 1, width - 2, width - 3, 4097, 4098, 4099, 8191, 20001]), 0, width)
+    say(f"topk odd row width {width}")
+    xd, ld = _upload(x, lens)
+    # positions at or past each length hold huge scores: never read, never chosen
+    for b, n in enumerate(lens):
+        xd[b, n:] = 1e30
     idx, vals = run_topk(lib, xd, ld, k)
     check_topk_exact(idx, vals, x, lens, k)

@@ -4,6 +4,8 @@ first-digit histogram equals the oracle's count over those logits exactly,
 the top-k is bit-exact against the oracle's top-k on the same float32 scores,
 and the histogram is all zero again afterwards (so the next call, or the next
 replay of a captured graph, starts clean)."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -164,7 +166,17 @@ def test_graph_replays_reset_the_histogram(lib):
         assert np.array_equal(eager.cpu().numpy().view(np.uint32), got.view(np.uint32)), rep
 
 
-@pytest.mark.parametrize("name", ["c2", "c3"])
+def _widened(name):
+    """A workload; "c3w" is c3 with 640 page slots per request (a row width of
+    40960: the top-k then runs its segment kernel), the extra slots unused."""
+    if name != "c3w":
+        return wl.generate(name)
+    inp = wl.generate("c3")
+    pad = np.full((inp.batch, 640 - inp.max_pages), wl.POISON, np.int32)
+    return dataclasses.replace(inp, page_table=np.concatenate([inp.page_table, pad], axis=1))
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c3w"])
 def test_histogram_that_does_not_belong_to_the_logits(lib, name):
     """topk_hist with a histogram that is not the one score_hist counted for
     these logits: all zero (a second topk_hist on the same logits, after the
@@ -174,7 +186,7 @@ def test_histogram_that_does_not_belong_to_the_logits(lib, name):
     import torch
 
     say(f"topk_hist with foreign histograms {name}")
-    inp = wl.generate(name)
+    inp = _widened(name)
     lens = inp.seq_lens.copy()
     k = inp.topk
     lens[:4] = [k + 1, min(4096, inp.max_c4), k - 1, 4097 if inp.max_c4 > 4097 else inp.max_c4]

@@ -1,8 +1,10 @@
 """The allocation-free top-k (dsa_indexer_topk_noalloc) through the C ABI:
 its output equals dsa_indexer_topk's with a caller workspace, bit for bit,
 on two calls in a row, the second with a smaller input, and on random rows
-that exercise its whole-row fallback. Sizes past its fixed array are refused
-on the host."""
+that exercise its whole-row fallback. The fixed array is the segment
+kernel's workspace, used only above a row width of 32768 positions, so those
+calls use wider rows (and the workloads of at most 32768 run alongside).
+Sizes past the array are refused on the host."""
 import numpy as np
 import pytest
 
@@ -32,8 +34,25 @@ def _same(ref_i, ref_v, got_i, got_v):
 
 
 def test_noalloc_equals_topk_on_two_calls_in_a_row(lib):
-    # the first call leaves the array holding c3's segments; the second, smaller
-    # input (c2: shorter rows, fewer requests) must not be affected by them
+    import torch
+
+    # the first call leaves the array holding 64 rows' segments; the second,
+    # smaller input (fewer requests, a narrower row width, shorter rows, another
+    # k) must not be affected by them
+    rng = np.random.default_rng(16)
+    for B, N, k in ((64, 65536, 2048), (16, 40000, 512)):
+        say(f"topk_noalloc vs topk on {B} random rows of width {N}, k={k}")
+        x = rng.standard_normal((B, N)).astype(np.float32)
+        lens = rng.integers(4097, N, size=B, endpoint=True).astype(np.int32)
+        lens[:3] = [N, k - 1, 4096]
+        xd = torch.from_numpy(x).cuda()
+        ld = torch.from_numpy(lens).cuda()
+        ref_i, ref_v, got_i, got_v = _both(lib, xd, ld, k)
+        _same(ref_i, ref_v, got_i, got_v)
+        check_topk_exact(got_i, got_v, x, lens, k)
+
+
+def test_noalloc_equals_topk_on_the_workloads(lib):
     for name in ("c3", "c2"):
         say(f"topk_noalloc vs topk on {name}")
         inp = wl.generate(name)
@@ -49,12 +68,12 @@ def test_noalloc_whole_row_paths(lib):
     import torch
 
     rng = np.random.default_rng(17)
-    B, N, k = 8, 20000, 300
+    B, N, k = 8, 40000, 300
     x = rng.standard_normal((B, N)).astype(np.float32)
     x[1] = 2.0                      # all equal: more candidates than a workgroup holds
     x[2, ::3] = np.nan
     x[3] = np.round(x[3] * 4) / 4   # heavy ties
-    lens = np.array([20000, 20000, 19999, 12345, 4097, 4096, 300, 0], np.int32)
+    lens = np.array([40000, 40000, 39999, 12345, 4097, 4096, 300, 0], np.int32)
     say("topk_noalloc whole-row paths")
     xd = torch.from_numpy(x).cuda()
     ld = torch.from_numpy(lens).cuda()
