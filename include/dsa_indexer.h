@@ -215,8 +215,8 @@ size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k
  *
  * One workgroup per request selects its row's top k. With max_c4 <= 32768 it
  * is the only kernel: a row longer than 4096 positions is held in registers,
- * cut at a sampled key (every 16th position), and the keys at or above the
- * cut become the candidates. With a wider row width, a segment kernel is
+ * cut at a key sampled from 64 runs of 32 positions, and the keys at or
+ * above the cut become the candidates. With a wider row width, a segment kernel is
  * enqueued first: it splits each row longer than 4096 positions into
  * segments of 4096 (up to 8 workgroups per request, each taking every 8th
  * segment from its own) and writes each segment's keys at or above a cut

@@ -86,10 +86,10 @@ constexpr int kSmallRanged = 16;              // the same, in the ranged select 
 // A row width of at most kRes positions needs no segment kernel: the row
 // kernel holds a whole row in registers (kResBlk blocks of kSeg positions,
 // four consecutive positions of each per lane) and cuts it itself, from
-// every kSampleStride-th position.
+// kSamples keys in 64 runs of 32 consecutive positions spread over the row.
 constexpr int kRes = 32768;
 constexpr int kResBlk = kRes / kSeg;
-constexpr int kSampleStride = 16;             // the sample: every 16th position
+constexpr int kSamples = 2 * kRowThreads;     // the sample: 64 runs of 32 positions
 static_assert(kSeg == 4 * kRowThreads, "a block of kSeg positions is one 16-byte group per lane");
 static_assert(2 * kBins <= kCap, "the sample histograms fit in cand_pos");
 
@@ -616,11 +616,12 @@ __device__ __forceinline__ Kth select_candidates(int n, int k, bool from_hist, u
 // narrow (the candidates above a cut share a few bins of the key's own first
 // digit, where the first pass would pile its LDS atomics onto a few words).
 // Returns r = 0xFFFFFFFF if fewer than k keys reach base (T < base: the caller
-// selects over the whole row). Out of line, like the whole-row path, so that
-// the common path's code stays as it is. The histograms are clear on entry,
+// selects over the whole row). Inline: as an out-of-line call it saved and
+// restored 40 registers per lane through scratch memory on every call (c3
+// top-k 14.56 -> 14.24 us inline). The histograms are clear on entry,
 // and rs.range is (0, 0), or with preset the count of candidates at or above
 // base and the largest key.
-__device__ __noinline__ Kth select_candidates_ranged(int n, int k, uint32_t base, bool preset) {
+__device__ __forceinline__ Kth select_candidates_ranged(int n, int k, uint32_t base, bool preset) {
   const int tid = threadIdx.x;
   if (!preset) {  // (else the gather left rs.range set)
     uint32_t hi = 0u, above = 0u;
@@ -902,11 +903,13 @@ __device__ __forceinline__ void block_scan_n(uint32_t (&v)[kN], uint32_t (&tot)[
 // select would otherwise sweep the candidates for.
 //
 // The cut: with the score kernel's histogram (hint, and wave 0's pick of it
-// in rs.hpick), that pick's bin edge. Otherwise the sample of every
-// kSampleStride-th position (n_s keys, held by every fourth lane) is counted
-// into a first-digit histogram, and the cut is the lower edge of the bin
-// holding its rank_s-th largest, rank_s = 1.1 m + 4 sqrt(m) + 4 for m = k n_s
-// / len the sample's expected share of the top k; a bin holding more than 32
+// in rs.hpick), that pick's bin edge. Otherwise a sample of n_s = kSamples
+// keys, 64 runs of 32 consecutive positions (one 128-byte line each) spread
+// evenly over the row and loaded by every wave before any of the row, so
+// that the cut is picked while the row is still arriving, is counted into a
+// first-digit histogram; the cut is the lower edge of the bin holding its
+// rank_s-th largest, rank_s = 1.1 m + 4 sqrt(m) + 4 for m = k n_s / len the
+// sample's expected share of the top k, and a bin holding more than 32
 // samples is split by a second digit over the samples in it. (On the c3
 // workload's rows longer than 4096: about 3000 candidates for k = 2048.) The
 // sample histograms live in rs.cand_pos, which the candidates overwrite
@@ -922,17 +925,24 @@ __device__ __forceinline__ int gather_resident(const float* row_ptr, int len, in
   // only positions [0, len) are readable through r1: a 16-byte load reaching
   // past len reads 0 for each word past it (the range is checked per word)
   const rsrc_t r1 = make_rsrc(row_ptr, (uint32_t)len * 4u);
-  u32x4 v[kResBlk];
-#pragma unroll
-  for (int j = 0; j < kResBlk; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(r1, (j * kSeg + 4 * tid) * 4, 0, 0);
+  // the sample first: 64 runs of 32 consecutive positions spread over the
+  // row (two positions per lane), so the cut is picked while the row arrives
+  const uint32_t run = (uint32_t)tid / 16u;
+  const uint32_t run0 = min((run * (uint32_t)len / 64u) & ~31u, (uint32_t)len - 32u);
+  const u32x2 sbits = __builtin_amdgcn_raw_buffer_load_b64(r1, (int)(run0 + 2u * ((uint32_t)tid & 15u)) * 4, 0, 0);
   const u32x4 zero4 = {0u, 0u, 0u, 0u};
   uint32_t* sample_hist = rs.cand_pos;  // two histograms of kBins
   *reinterpret_cast<u32x4*>(sample_hist + 4 * tid) = zero4;
   static_assert(4 * kRowThreads == 2 * kBins, "one 16-byte store per lane clears both");
+  // (the barrier does not wait for loads: every wave's sample load is issued
+  // before any row load, so the samples come back first)
   __syncthreads();
+  u32x4 v[kResBlk];
+#pragma unroll
+  for (int j = 0; j < kResBlk; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(r1, (j * kSeg + 4 * tid) * 4, 0, 0);
 
   uint32_t lo;
-  const uint32_t n_s = (uint32_t)(len + kSampleStride - 1) / kSampleStride;
+  const uint32_t n_s = kSamples;
   const float m = (float)k * (float)n_s / (float)len;
   const float want = 1.1f * m + 4.0f * sqrtf(m) + 4.0f;
   if (hint && rs.hpick[2] != 0u) {
@@ -941,31 +951,18 @@ __device__ __forceinline__ int gather_resident(const float* row_ptr, int len, in
     lo = 1u;  // every valid key
   } else {
     const uint32_t rank_s = (uint32_t)want;  // 1 .. n_s - 1
-    // this lane's sampled keys (lanes 4i: position 16i of every block), 0 if none
-    constexpr int kPerBlk = kSeg / kSampleStride / (kRowThreads / 4);
-    static_assert(kPerBlk == 1, "one sampled position per block in every fourth lane");
-    uint32_t sk[kResBlk];
+    const uint32_t sk[2] = {order_key(__uint_as_float(sbits.x)), order_key(__uint_as_float(sbits.y))};
 #pragma unroll
-    for (int j = 0; j < kResBlk; ++j) {
-      const bool in = (tid & 3) == 0 && j * kSeg + 4 * tid < len;
-      sk[j] = in ? order_key(__uint_as_float(v[j][0])) : 0u;
-    }
-    if ((tid & 3) == 0) {
-#pragma unroll
-      for (int j = 0; j < kResBlk; ++j)
-        if (sk[j] != 0u) atomicAdd(&sample_hist[hslot(sk[j] >> 21)], 1u);
-    }
+    for (int i = 0; i < 2; ++i) atomicAdd(&sample_hist[hslot(sk[i] >> 21)], 1u);
     __syncthreads();
     block_pick<kBins>(sample_hist, [&](uint32_t) { return rank_s; });  // the total is n_s
     const uint32_t b0 = rs.bcast[0], above = rs.bcast[1], in_bin = rs.bcast[2];
     lo = b0 << 21;
     if (in_bin > 32u) {
       uint32_t* h2 = sample_hist + kBins;
-      if ((tid & 3) == 0) {
 #pragma unroll
-        for (int j = 0; j < kResBlk; ++j)
-          if (sk[j] != 0u && (sk[j] >> 21) == b0) atomicAdd(&h2[hslot((sk[j] >> 10) & 0x7FFu)], 1u);
-      }
+      for (int i = 0; i < 2; ++i)
+        if ((sk[i] >> 21) == b0) atomicAdd(&h2[hslot((sk[i] >> 10) & 0x7FFu)], 1u);
       __syncthreads();
       block_pick<kBins>(h2, [&](uint32_t) { return rank_s - above; });
       lo |= rs.bcast[0] << 10;
