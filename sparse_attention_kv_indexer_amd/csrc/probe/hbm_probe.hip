@@ -1,10 +1,11 @@
 // HBM read probes for the bench: what the chip delivers for
 //   (a) one long contiguous read, and
-//   (b) random 8 KiB pages read the way the score kernel reads its keys: a
-//       fixed grid of one-wave workgroups, each over an equal contiguous range
-//       of a page-id list, eight 1 KiB wave loads per page (non-temporal),
-//       two pages in flight per wave, and nothing else (no page-table walk,
-//       no compute, no stores but one word per lane at the end).
+//   (b) random pages of 8 KiB (bf16 keys) or 4 KiB (fp8 codes) read the way
+//       the score kernel reads its keys: a fixed grid of one-wave workgroups,
+//       each over an equal contiguous range of a page-id list, 1 KiB wave
+//       loads (non-temporal), two pages in flight per wave, and nothing else
+//       (no page-table walk, no scales, no compute, no stores but one word
+//       per lane at the end).
 // They measure the ceiling of the access pattern, not a step of the method.
 // Each wave folds what it read into one word per lane, so no load is dead.
 // Every access goes through a buffer resource sized to its buffer, so nothing
@@ -46,9 +47,10 @@ __global__ __launch_bounds__(256) void stream_read(const void* src, uint32_t chu
 }
 
 // (b) random pages: workgroup g reads pages ids[g * per .. min(n_ids, (g + 1) * per)).
+template <int kPageBytes>
 __global__ __launch_bounds__(64) void page_read(const void* pool, uint32_t pool_bytes, const int32_t* ids,
                                                 int32_t n_ids, uint32_t* out) {
-  constexpr int kPageBytes = 8192, kLoads = kPageBytes / 1024;
+  constexpr int kLoads = kPageBytes / 1024;
   const int lane = threadIdx.x;
   const int per = (n_ids + (int)gridDim.x - 1) / (int)gridDim.x;
   const int s = min(n_ids, (int)blockIdx.x * per), e = min(n_ids, s + per);
@@ -110,12 +112,18 @@ extern "C" int dsa_probe_stream_read(const void* src, uint64_t bytes, uint32_t* 
   return (int)hipGetLastError();
 }
 
-// pool: pool_bytes of 8 KiB pages (below 4 GiB); ids: n_ids page ids (an id
-// outside the pool reads nothing); out: grid * 64 words. Returns a hipError_t.
+// pool: pool_bytes of pages of page_bytes (8192 or 4096; below 4 GiB in
+// all); ids: n_ids page ids (an id outside the pool reads nothing); out:
+// grid * 64 words. Returns a hipError_t.
 extern "C" int dsa_probe_page_read(const void* pool, uint64_t pool_bytes, const int32_t* ids, int n_ids, uint32_t* out,
-                                   int grid, hipStream_t stream) {
+                                   int grid, int page_bytes, hipStream_t stream) {
   if (!pool || !ids || !out || grid < 1 || n_ids < 1 || pool_bytes >= (uint64_t(1) << 32))
     return (int)hipErrorInvalidValue;
-  hipLaunchKernelGGL(page_read, dim3(grid), dim3(64), 0, stream, pool, (uint32_t)pool_bytes, ids, n_ids, out);
+  if (page_bytes == 8192)
+    hipLaunchKernelGGL(page_read<8192>, dim3(grid), dim3(64), 0, stream, pool, (uint32_t)pool_bytes, ids, n_ids, out);
+  else if (page_bytes == 4096)
+    hipLaunchKernelGGL(page_read<4096>, dim3(grid), dim3(64), 0, stream, pool, (uint32_t)pool_bytes, ids, n_ids, out);
+  else
+    return (int)hipErrorInvalidValue;
   return (int)hipGetLastError();
 }
