@@ -7,12 +7,13 @@
 // all heads (the first 512 dims are the value). The latents sit in pages of
 // 64 positions, found through the same page table as the indexer keys.
 //
-// attention_kernel: one 256-thread workgroup per (request, split), where a
-// split is a run of at most `chunk` entries of the request's list, on one CU.
-// It processes tiles of 32 positions:
-//   - staging: direct-to-LDS loads (global_load_lds_dwordx4) into four tile
-//     buffers, up to four tiles ahead. Rows are stored as 72 chunks of 16 B,
-//     with chunk c of row r at c ^ swz(r);
+// attention_kernel: one 512-thread workgroup per (request, split), where a
+// split is a run of at most `chunk` entries of the request's list, on one CU:
+// four compute waves and four loader waves, two waves per SIMD. It processes
+// tiles of 32 positions:
+//   - staging (the loader waves): direct-to-LDS loads (global_load_lds_dwordx4)
+//     into four tile buffers, up to four tiles ahead. Rows are stored as 72
+//     chunks of 16 B, with chunk c of row r at c ^ swz(r);
 //   - scores: wave (ph, hh) computes the 16 positions x 16 heads block
 //     (positions 16ph.., heads 16hh..) of S^T over the 576 dims with
 //     v_mfma_f32_16x16x32_bf16 (its 16 heads' queries held in registers) and
@@ -51,7 +52,8 @@ constexpr int kTileBytes = kTile * kLatBytes;  // 36 KiB
 constexpr int kBufs = 4;                       // staged tiles: one computed, three loading
 constexpr int kSRow = 36;                      // floats per row (head) of the score tile: 32 + padding
 constexpr int kSTile = kAttHeads * kSRow;
-constexpr int kAttThreads = 256;
+constexpr int kWorkThreads = 256;             // the four compute waves
+constexpr int kAttThreads = 2 * kWorkThreads;  // and four loader waves
 constexpr int kQSteps = kKD / 32;              // 18 k-steps of the 16x16x32 MFMA
 constexpr int kStage = kLatBytes / 128;        // 9 loads of 16 B per thread per tile
 constexpr int kMergeThreads = 256;
@@ -63,7 +65,7 @@ constexpr float kRegrow = 8.0f;                // log2 headroom of the weights o
 constexpr float kLn2 = 0.693147180559945309f;
 
 static_assert(kStage * 128 == kLatBytes, "a row is 8 threads x kStage x 16 B");
-static_assert(kTile * 8 == kAttThreads, "8 threads stage each row of a tile");
+static_assert(kTile * 8 == kWorkThreads, "8 loader lanes stage each row of a tile");
 static_assert(kMaxAttChunk % kTile == 0, "splits are whole tiles");
 
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -159,7 +161,7 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t lds) {
 // and no LDS operations of this wave are outstanding.
 constexpr int vm_lgkm_wait(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (0 << 8); }
 
-__global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kAttThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void attention_kernel(const AttArgs a) {
   // Tile t is staged in buffer t % 4 while tiles t+1 .. t+3 are loading.
   __shared__ __attribute__((aligned(16))) unsigned char tbuf[kBufs * kTileBytes];
@@ -171,6 +173,7 @@ void attention_kernel(const AttArgs a) {
   att_place(a.nsplit, b, s);
   if (b >= a.batch) return;
   const int tid = (int)threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const bool loader = wv >= kWorkThreads / 64;  // waves 4..7 only stage tiles
   const int g0 = s * a.chunk;
   const int n = min(a.chunk, a.k - g0);  // list entries of this split, >= 1
   const int ntiles = (n + kTile - 1) / kTile;
@@ -180,9 +183,11 @@ void attention_kernel(const AttArgs a) {
   const int g = lane >> 4, j = lane & 15;
   const rsrc_t qr = make_rsrc(a.q + (int64_t)b * kAttHeads * kKD, kAttHeads * kLatBytes);
   u32x4 qv[kQSteps];  // queries of head 16(wv >> 1) + j, k-slots 8g.. of each 32-dim step
+  if (!loader) {
 #pragma unroll
-  for (int st = 0; st < kQSteps; ++st)
-    qv[st] = __builtin_amdgcn_raw_buffer_load_b128(qr, (16 * (wv >> 1) + j) * kLatBytes + (4 * st + g) * 16, 0, 0);
+    for (int st = 0; st < kQSteps; ++st)
+      qv[st] = __builtin_amdgcn_raw_buffer_load_b128(qr, (16 * (wv >> 1) + j) * kLatBytes + (4 * st + g) * 16, 0, 0);
+  }
 
   // Resolve every entry of the split to a pool row (page * 64 + slot row).
   const rsrc_t ir = make_rsrc(a.idx + (int64_t)b * a.k, (uint32_t)a.k * 4u);
@@ -221,20 +226,21 @@ void attention_kernel(const AttArgs a) {
   }
   bad = __syncthreads_or(bad);  // also publishes rows[]
 
-  // Staging with direct-to-LDS loads: wave wv's load i fills LDS chunks
-  // 64(9wv + i) .. +63 of the tile (lane -> +lane). LDS chunk L is row L / 72,
-  // stored position L % 72, which holds row chunk (L % 72) ^ swz(row).
+  // Staging with direct-to-LDS loads: loader wave lw's load i fills LDS
+  // chunks 64(9lw + i) .. +63 of the tile (lane -> +lane). LDS chunk L is row
+  // L / 72, stored position L % 72, which holds row chunk (L % 72) ^ swz(row).
+  const int lw = wv & 3;
   int drow[kStage], dsrc[kStage];
 #pragma unroll
   for (int i = 0; i < kStage; ++i) {
-    const int L = 64 * (kStage * wv + i) + lane;
+    const int L = 64 * (kStage * lw + i) + lane;
     const int r = L / 72, p = L % 72;
     drow[i] = r;
     dsrc[i] = ((p & ~7) | ((p & 7) ^ swz(r))) * 16;
   }
   const unsigned char* kvb = reinterpret_cast<const unsigned char*>(a.kv);
   const uint32_t lds_tiles =
-      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)tbuf + 1024u * kStage * wv;
+      (uint32_t)(uintptr_t)(__attribute__((address_space(3))) unsigned char*)tbuf + 1024u * kStage * lw;
   auto stage = [&](int buf, int t) {
     uint32_t v[kStage];
 #pragma unroll
@@ -359,18 +365,22 @@ void attention_kernel(const AttArgs a) {
     }
   };
 
-  // Software pipeline over the tiles, one barrier per step. Step t: the
-  // softmax of tile t (its scores were published in step t-1), the scores of
-  // tile t+1 and the values of tile t, three independent streams the
-  // compiler interleaves; then wait for this wave's loads of tile t+2 and its
-  // LDS accesses, barrier (tile t+1's scores are complete, tile t+2 has
-  // landed, every wave is done with tile t), and refill tile t's buffer with
-  // tile t+4. The prologue loads tiles 0..3 and publishes tile 0's scores.
+  // Software pipeline over the tiles, one barrier per step, in which the
+  // loader waves and the compute waves meet. Compute step t: the softmax of
+  // tile t (its scores were published in step t-1), the scores of tile t+1
+  // and the values of tile t, three independent streams the compiler
+  // interleaves; then its LDS accesses are waited for and the barrier
+  // follows. Loader step t: wait for its loads of tile t+2, the barrier (tile
+  // t+1's scores are complete, tile t+2 has landed, every wave is done with
+  // tile t), then refill tile t's buffer with tile t+4. The prologue loads
+  // tiles 0..3 and publishes tile 0's scores. (Issuing the loads from the
+  // compute waves stalled them on the memory pipeline's back-pressure, about
+  // 950 cycles per tile.) Both roles pass the same 2 + ntiles barriers.
   auto tbuf_of = [&](int t) { return tbuf + (t & (kBufs - 1)) * kTileBytes; };
-  __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));  // the queries have landed; only tile loads are outstanding below
-  for (int t = 0; t < kBufs && t < ntiles; ++t) stage(t, t);
-  {
-    const int later = min(kBufs, ntiles) - 1;  // tiles 1.. already loading
+  const int later = min(kBufs, ntiles) - 1;  // tiles 1.. loading in the prologue
+  if (loader) {
+    for (int t = 0; t < kBufs && t < ntiles; ++t) stage(t, t);
+    // tile 0 has landed
     if (later >= 3)
       __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(3 * kStage));
     else if (later == 2)
@@ -380,7 +390,7 @@ void attention_kernel(const AttArgs a) {
     else
       __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
     __builtin_amdgcn_s_barrier();
-    scores(tbuf_of(0), 0);
+    // tile 1 has landed
     if (later >= 3)
       __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(2 * kStage));
     else if (later == 2)
@@ -388,19 +398,29 @@ void attention_kernel(const AttArgs a) {
     else
       __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
     __builtin_amdgcn_s_barrier();
+    for (int t = 0; t < ntiles; ++t) {
+      // tile t+2 must have landed; tile t+3's loads may still be in flight
+      if (t + 3 < ntiles)
+        __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(kStage));
+      else
+        __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+      __builtin_amdgcn_s_barrier();
+      if (t + kBufs < ntiles) stage(t & (kBufs - 1), t + kBufs);
+    }
+    return;
   }
+  __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));  // the queries have landed
+  __builtin_amdgcn_s_barrier();
+  scores(tbuf_of(0), 0);
+  __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+  __builtin_amdgcn_s_barrier();
   for (int t = 0; t < ntiles; ++t) {
     u32x4 P[2];
     softmax(t, P);
     if (t + 1 < ntiles) scores(tbuf_of(t + 1), t + 1);
     values(tbuf_of(t), P);
-    // tile t+2 must have landed; tile t+3's loads may still be in flight
-    if (t + 3 < ntiles)
-      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(kStage));
-    else
-      __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
+    __builtin_amdgcn_s_waitcnt(vm_lgkm_wait(0));
     __builtin_amdgcn_s_barrier();
-    if (t + kBufs < ntiles) stage(t & (kBufs - 1), t + kBufs);
   }
 
   // Sums of weights of this lane's two heads over all lanes (g) of the wave.
