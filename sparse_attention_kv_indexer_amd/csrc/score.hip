@@ -117,12 +117,14 @@ struct Window {
   int b0;
   uint32_t cnt, pre, tot, acc;
 };
-__device__ __forceinline__ void window_load(Window& W, const Shape& sh, bool tail) {
-  const RowWork r = row_work(sh, W.b0 + (int)(threadIdx.x & 63));
+__device__ __forceinline__ void window_set(Window& W, const RowWork& r, bool tail) {
   W.cnt = tail ? r.chunks : r.pages;
   const uint32_t incl = wave_inclusive_scan(W.cnt);
   W.pre = incl - W.cnt;
   W.tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+}
+__device__ __forceinline__ void window_load(Window& W, const Shape& sh, bool tail) {
+  window_set(W, row_work(sh, W.b0 + (int)(threadIdx.x & 63)), tail);
 }
 // Moves W forward to the window holding `item` (an index into its list, below
 // the list total) and returns the request and the index inside the request.
@@ -209,8 +211,10 @@ void score_kernel(
   // list totals, then this workgroup's contiguous ranges: pages [s, pe) and
   // tail chunks [ts, te)
   uint32_t n_pages = 0, n_chunks = 0;
+  RowWork first{0, 0, 0, 0};  // the first window's requests, kept: no second round trip for them
   for (int b0 = 0; b0 < batch; b0 += 64) {
     const RowWork r = row_work(sh, b0 + lane);
+    if (b0 == 0) first = r;
     n_pages += wave_total(r.pages);
     n_chunks += wave_total(r.chunks);
   }
@@ -280,7 +284,7 @@ void score_kernel(
 
   if (s < pe) {
     Window W{0, 0, 0, 0, 0};
-    window_load(W, sh, false);
+    window_set(W, first, false);
 
     // Three-stage pipeline over the range: while item `it` is computed, the
     // key page of item it + 1 and the page id of item it + 2 are in flight.
@@ -508,7 +512,7 @@ void score_kernel(
   if (ts < te) {
     // -inf tail chunks
     Window W{0, 0, 0, 0, 0};
-    window_load(W, sh, true);
+    window_set(W, first, true);
     const u32x4 ninf = {0xFF800000u, 0xFF800000u, 0xFF800000u, 0xFF800000u};
     for (uint32_t it = ts; it < te; ++it) {
       int b;
