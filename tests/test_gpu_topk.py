@@ -265,3 +265,44 @@ def test_odd_row_widths(lib, width):
         xd[b, n:] = 1e30
     idx, vals = run_topk(lib, xd, ld, k)
     check_topk_exact(idx, vals, x, lens, k)
+
+
+def test_resident_rows_ties_zeros_nan_inf(lib):
+    """Rows held in registers (longer than 4096 positions, row width at most
+    32768) with the special values: heavy ties, -0 and +0, NaN ranked last,
+    -inf, all equal, all NaN, and NaN at the sampled runs."""
+    rng = np.random.default_rng(22)
+    B, N, k = 8, 20000, 2000
+    x = rng.integers(-3, 4, size=(B, N)).astype(np.float32)  # 7 distinct values
+    x[1] = 0.0
+    x[1, ::3] = -0.0
+    x[2, :] = 1.5
+    x[3, 10:19000:7] = np.nan
+    x[4, ::5] = -np.inf
+    x[5, :] = np.nan
+    x[6] = rng.standard_normal(N).astype(np.float32)
+    x[6, ::16] = np.nan  # every sampled run holds NaN
+    x[7] = -np.inf
+    x[7, 12345] = 3.0
+    lens = np.array([20000, 19999, 18000, 19000, 15001, 9000, 20000, 20000])
+    say("topk resident rows: ties, zeros, nan, inf")
+    xd, ld = _upload(x, lens)
+    idx, vals = run_topk(lib, xd, ld, k)
+    check_topk_exact(idx, vals, x, lens, k)
+    assert idx[2].tolist() == list(range(k))
+    assert idx[5].tolist() == list(range(k))
+
+
+@pytest.mark.parametrize("k", [15356, 16000, 32767])
+def test_resident_rows_with_k_past_the_candidate_capacity(lib, k):
+    """k at and past what a row workgroup holds in LDS (15,356 candidates):
+    the rows are selected over whole, at a row width held in registers, next
+    to a row of exactly k + 1 positions and one shorter than k."""
+    rng = np.random.default_rng(k)
+    B, N = 4, 32768
+    x = rng.standard_normal((B, N)).astype(np.float32)
+    lens = np.array([32768, min(k + 1, N), k - 1, 30000])
+    say(f"topk resident rows, k={k}")
+    xd, ld = _upload(x, lens)
+    idx, vals = run_topk(lib, xd, ld, k)
+    check_topk_exact(idx, vals, x, lens, k)
