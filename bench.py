@@ -127,7 +127,7 @@ def algorithmic_bytes(inp, hwm: bool, tokens: int = 1, token_lens=None) -> dict:
     pages = wl.pages_needed(lens)
     per_key = wl.DIM + 4 if inp.fp8 else wl.DIM * 2  # fp8: 64 codes and a float32 scale
     k_bytes = int(pages.sum()) * wl.PAGE * per_key
-    out_positions = tokens * inp.batch * inp.max_c4 if not hwm else int((pages * wl.PAGE).sum())
+    out_positions = tokens * (inp.batch * inp.max_c4 if not hwm else int((pages * wl.PAGE).sum()))
     out_bytes = out_positions * 4
     table_bytes = int(pages.sum()) * 4
     req_bytes = inp.batch * tokens * (wl.HEADS * wl.DIM * 2 + wl.HEADS * 4 + 4)
@@ -364,7 +364,7 @@ def measure_step(cfg_name: str, steps: int, warmup: int, hwm=False, keys="bf16",
     def launch_score(t):
         if T > 1:
             binding.score_mtp(t["q"], t["w"], t["k_pool"], t["page_table"], t["seq_lens"],
-                              out=t["logits"].view(B, T, N))
+                              out=t["logits"].view(B, T, N), row_hwm=t["hwm"])
         elif inp.fp8:
             binding.score_fp8(t["q"], t["w"], t["k8"], t["k_scale"], t["page_table"], t["seq_lens"], out=t["logits"],
                               row_hwm=t["hwm"])
@@ -489,8 +489,8 @@ def main():
     cfg = wl.CONFIGS[args.config]
     T = args.tokens
     if args.stage == "indexer" and not args.probe and not args.copy_calibration:
-        if T != 1 and (args.keys == "fp8" or args.hwm or not 1 <= T <= 4):
-            print("bench.py: --tokens 2..4 runs bf16 keys with the stateless tail", file=sys.stderr)
+        if T != 1 and (args.keys == "fp8" or not 1 <= T <= 4):
+            print("bench.py: --tokens 2..4 runs bf16 keys", file=sys.stderr)
             sys.exit(2)
         if args.topk == "hist" and (T != 1 or args.keys == "fp8"):
             print("bench.py: --topk hist runs one query token with bf16 keys", file=sys.stderr)

@@ -51,7 +51,7 @@
 extern "C" {
 #endif
 
-#define DSA_INDEXER_ABI_VERSION 6
+#define DSA_INDEXER_ABI_VERSION 7
 #define DSA_INDEXER_HEADS 32 /* indexer heads */
 #define DSA_INDEXER_DIM 64   /* head dimension */
 #define DSA_INDEXER_PAGE 64  /* c4 positions per page */
@@ -166,8 +166,7 @@ int dsa_indexer_score_fp8(const void *q, const float *w, const void *k_pool_fp8,
  * causal length seq_lens[b][t] (clamped to [0, max_pages * 64]):
  *   logits[b][t][s] = sum_h w[b][t][h] * max(0, q[b][t][h] . k[s])   for s < seq_lens[b][t]
  * and -inf for s >= seq_lens[b][t]. Each key page below the longest of a
- * request's lengths is read once for all its tokens; the -inf tail is
- * written in full on every call (the stateless mode). The logits rows are
+ * request's lengths is read once for all its tokens. The logits rows are
  * [batch * tokens][max_pages * 64], so dsa_indexer_topk with batch * tokens
  * rows and the same seq_lens selects per token.
  *
@@ -177,12 +176,21 @@ int dsa_indexer_score_fp8(const void *q, const float *w, const void *k_pool_fp8,
  *   seq_lens   int32 [batch][tokens]
  *   batch      1 .. 65535;  tokens 1 .. 4;  batch * tokens * max_pages <= 2^26
  *   logits     fp32  [batch][tokens][max_pages * 64], 16-byte aligned
+ *   row_hwm    NULL (every call writes the whole -inf tail of every token's
+ *              row), or int32 [batch] high-water marks for the incremental
+ *              tail, one per request for all its tokens: as for
+ *              dsa_indexer_score with L_b = the longest of the request's
+ *              clamped lengths. The caller guarantees on entry that
+ *              logits[b][t][s] == -inf for every t and every s >= row_hwm[b];
+ *              the call rewrites -inf only on pages in [L_b, row_hwm[b]) of
+ *              every token's row and sets row_hwm[b] = L_b. The result is
+ *              identical in both modes.
  *
  * Errors and device-side conventions as for dsa_indexer_score.
  */
 int dsa_indexer_score_mtp(const void *q, const float *w, const void *k_pool, int64_t num_pages,
                           const int32_t *page_table, const int32_t *seq_lens, int32_t batch, int32_t tokens,
-                          int32_t max_pages, float *logits, hipStream_t stream);
+                          int32_t max_pages, float *logits, int32_t *row_hwm, hipStream_t stream);
 
 /* Bytes of device workspace dsa_indexer_topk needs for these sizes: 0 when
  * max_c4 <= 32768 (the workspace may then be NULL) or the sizes are out of

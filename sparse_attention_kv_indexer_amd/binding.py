@@ -59,7 +59,7 @@ def load() -> ctypes.CDLL:
     lib.dsa_indexer_score_fp8.restype = ctypes.c_int
     lib.dsa_indexer_score_fp8.argtypes = [vp, vp, vp, vp, i64, vp, vp, i32, i32, vp, vp, vp]
     lib.dsa_indexer_score_mtp.restype = ctypes.c_int
-    lib.dsa_indexer_score_mtp.argtypes = [vp, vp, vp, i64, vp, vp, i32, i32, i32, vp, vp]
+    lib.dsa_indexer_score_mtp.argtypes = [vp, vp, vp, i64, vp, vp, i32, i32, i32, vp, vp, vp]
     lib.dsa_indexer_topk_workspace_bytes.restype = sz
     lib.dsa_indexer_topk_workspace_bytes.argtypes = [i32, i32, i32]
     lib.dsa_indexer_topk.restype = ctypes.c_int
@@ -205,12 +205,14 @@ def score_fp8(q, w, k8, k_scale, page_table, seq_lens, out=None, row_hwm=None, s
     return out
 
 
-def score_mtp(q, w, k_pool, page_table, seq_lens, out=None, stream=None):
+def score_mtp(q, w, k_pool, page_table, seq_lens, out=None, row_hwm=None, stream=None):
     """Logits [B, T, max_pages*64] (float32) for T query tokens per request.
 
     q bf16 [B,T,32,64]; w float32 [B,T,32]; k_pool bf16 [num_pages,64,64];
     page_table int32 [B,max_pages]; seq_lens int32 [B,T] (each token's
     length); ``out`` float32 [B,T,max_pages*64] is allocated when not given.
+    ``row_hwm`` int32 [B] (one mark per request) selects the incremental tail
+    (the caller keeps ``out`` and ``row_hwm`` across calls).
     """
     import torch
 
@@ -230,9 +232,11 @@ def score_mtp(q, w, k_pool, page_table, seq_lens, out=None, stream=None):
     if out is None:
         out = torch.empty((B, T, S * PAGE), dtype=torch.float32, device=dev)
     _check(out, "out", (torch.float32,), (B, T, S * PAGE), dev)
+    if row_hwm is not None:
+        _check(row_hwm, "row_hwm", (torch.int32,), (B,), dev)
     st = load().dsa_indexer_score_mtp(
         q.data_ptr(), w.data_ptr(), k_pool.data_ptr(), k_pool.shape[0], page_table.data_ptr(), seq_lens.data_ptr(),
-        B, T, S, out.data_ptr(), _stream_ptr(stream))
+        B, T, S, out.data_ptr(), row_hwm.data_ptr() if row_hwm is not None else None, _stream_ptr(stream))
     if st != 0:
         raise DsaError(st, "dsa_indexer_score_mtp")
     return out

@@ -95,16 +95,16 @@ int dsa_indexer_score_fp8(const void* q, const float* w, const void* k_pool_fp8,
 
 int dsa_indexer_score_mtp(const void* q, const float* w, const void* k_pool, int64_t num_pages,
                           const int32_t* page_table, const int32_t* seq_lens, int32_t batch, int32_t tokens,
-                          int32_t max_pages, float* logits, hipStream_t stream) {
+                          int32_t max_pages, float* logits, int32_t* row_hwm, hipStream_t stream) {
   if (!q || !w || !k_pool || !page_table || !seq_lens || !logits) return DSA_ERR_NULL;
   if (batch < 1 || batch > kMaxBatch || tokens < 1 || tokens > dsa::kMaxTokens || max_pages < 1 ||
       max_pages > kMaxPages || num_pages < 1 || (int64_t)batch * tokens * max_pages > kMaxSlots)
     return DSA_ERR_SHAPE;
   if (misaligned16(q) || misaligned16(w) || misaligned16(k_pool) || misaligned16(logits) ||
-      misaligned4(page_table) || misaligned4(seq_lens))
+      misaligned4(page_table) || misaligned4(seq_lens) || misaligned4(row_hwm))
     return DSA_ERR_ALIGN;
   return from_hip(dsa::launch_score(q, w, k_pool, nullptr, num_pages, page_table, seq_lens, batch, tokens, max_pages,
-                                    logits, nullptr, nullptr, stream));
+                                    logits, row_hwm, nullptr, stream));
 }
 
 size_t dsa_indexer_topk_workspace_bytes(int32_t batch, int32_t max_c4, int32_t k) {

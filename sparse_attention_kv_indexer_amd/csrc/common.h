@@ -57,14 +57,14 @@ constexpr int32_t kMaxRowPositions = 1 << 28;
 // on this thread and returns DSA_ERR_HIP.
 int record_hip_error(hipError_t e);
 
-// Enqueue the score kernel (and, with row_hwm, the high-water-mark update).
+// Enqueue the score kernel (with row_hwm, the incremental -inf tail: one mark
+// per request, the longest of its tokens' lengths).
 // hist: nullptr, or uint32 [B][kHistBins] to which the kernel adds, for every
 // valid position of request b, one count in bin order_key(score) >> kHistShift
 // (tokens == 1 only).
 // k_scale == nullptr: bfloat16 keys; otherwise e4m3fn keys with these per-key
 // scales (tokens == 1). tokens (1..4) query tokens per request: q [B][tokens][32][64],
-// w [B][tokens][32], seq_lens [B][tokens], logits [B][tokens][width];
-// row_hwm only with tokens == 1.
+// w [B][tokens][32], seq_lens [B][tokens], logits [B][tokens][width].
 constexpr int32_t kMaxTokens = 4;
 hipError_t launch_score(const void* q, const float* w, const void* k_pool, const float* k_scale,
                         int64_t num_pages, const int32_t* page_table, const int32_t* seq_lens, int32_t batch,

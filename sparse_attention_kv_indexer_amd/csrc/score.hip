@@ -194,7 +194,7 @@ void score_kernel(
     const int32_t* __restrict__ seq_lens,    // [B][kTok]
     int32_t batch, int32_t max_pages,
     float* __restrict__ logits,              // [B][kTok][max_pages * 64]
-    int32_t* __restrict__ row_hwm,           // [B] or null (kTok == 1 only)
+    int32_t* __restrict__ row_hwm,           // [B] or null: the longest of each request's token lengths
     uint32_t* __restrict__ hist)             // [B][kHistBins] or null (kTok == 1 only)
 {
   const int lane = threadIdx.x;
@@ -206,7 +206,7 @@ void score_kernel(
   // loads it would use instead wait for every page load in flight)
   const Shape sh{make_rsrc(seq_lens, (uint32_t)(batch * kTok) * 4u),
                  make_rsrc(row_hwm, row_hwm != nullptr ? (uint32_t)batch * 4u : 0u),
-                 kTok == 1 && row_hwm != nullptr, batch, max_pages * kPage, kTok};
+                 row_hwm != nullptr, batch, max_pages * kPage, kTok};
 
   // list totals, then this workgroup's contiguous ranges: pages [s, pe) and
   // tail chunks [ts, te)
@@ -593,15 +593,15 @@ hipError_t launch_score(const void* q, const float* w, const void* k_pool, const
         break;
       case 2:
         launch_variant<false, 2>(grid, stream, q, w, k_pool, k_scale, num_pages, page_table, seq_lens, batch,
-                                 max_pages, logits, nullptr, nullptr);
+                                 max_pages, logits, row_hwm, nullptr);
         break;
       case 3:
         launch_variant<false, 3>(grid, stream, q, w, k_pool, k_scale, num_pages, page_table, seq_lens, batch,
-                                 max_pages, logits, nullptr, nullptr);
+                                 max_pages, logits, row_hwm, nullptr);
         break;
       default:
         launch_variant<false, 4>(grid, stream, q, w, k_pool, k_scale, num_pages, page_table, seq_lens, batch,
-                                 max_pages, logits, nullptr, nullptr);
+                                 max_pages, logits, row_hwm, nullptr);
         break;
     }
   }

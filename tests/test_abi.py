@@ -35,7 +35,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_version_and_status_strings(lib):
-    assert lib.dsa_indexer_abi_version() == 6
+    assert lib.dsa_indexer_abi_version() == 7
     for st in (OK, NULL, SHAPE, ALIGN, K, WS, -6, SCRATCH):
         assert lib.dsa_indexer_status_string(st).decode() not in ("", "unknown status")
     assert lib.dsa_indexer_status_string(12345).decode() == "unknown status"
@@ -197,7 +197,7 @@ def test_attention_workspace_contract(lib):
 
 def mtp_args(**over):
     args = dict(q=A, w=A, k_pool=A, num_pages=4, page_table=A, seq_lens=A, batch=2, tokens=2, max_pages=3, logits=A,
-                stream=None)
+                row_hwm=None, stream=None)
     args.update(over)
     return list(args.values())
 
@@ -214,7 +214,8 @@ def test_score_mtp_shape(lib, over):
     assert lib.dsa_indexer_score_mtp(*mtp_args(**over)) == SHAPE
 
 
-@pytest.mark.parametrize("field,off", [("q", 8), ("w", 4), ("k_pool", 2), ("logits", 4), ("page_table", 2), ("seq_lens", 1)])
+@pytest.mark.parametrize("field,off", [("q", 8), ("w", 4), ("k_pool", 2), ("logits", 4), ("page_table", 2), ("seq_lens", 1),
+                                       ("row_hwm", 2)])
 def test_score_mtp_alignment(lib, field, off):
     assert lib.dsa_indexer_score_mtp(*mtp_args(**{field: A + off})) == ALIGN
 

@@ -98,3 +98,44 @@ def test_each_token_matches_the_single_token_kernel(lib, tokens):
         one = lib.score(q, w, t["k_pool"], t["page_table"], lens)
         torch.cuda.synchronize()
         assert np.array_equal(one.cpu().numpy(), got[:, tt], equal_nan=True), f"token {tt}"
+
+
+@pytest.mark.parametrize("tokens", [2, 3, 4])
+def test_incremental_tail_follows_lengths(lib, tokens):
+    """The incremental -inf tail with several query tokens (one mark per
+    request, the longest of its tokens' lengths): over a sequence of calls
+    whose lengths grow, shrink, drop to zero and return to full, the kept
+    logits equal a stateless call's bit for bit at every step, and the marks
+    hold the longest length of each request."""
+    import torch
+
+    B, S, T = 9, 40, tokens
+    N = S * 64
+    inp = wl.random_case(400 + tokens, B, S, lens=[N] * B)  # the pool backs every page
+    mt = wl.mtp_inputs(inp, T, tokens)
+    t = lib.to_device(inp)
+    q = torch.from_numpy(np.ascontiguousarray(mt.q_bits).view("int16")).cuda().view(torch.bfloat16)
+    w = torch.from_numpy(np.ascontiguousarray(mt.w)).cuda()
+    kept = torch.full((B, T, N), float("-inf"), dtype=torch.float32, device="cuda")
+    hwm = torch.zeros(B, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(tokens)
+    base = rng.integers(0, N, size=B, endpoint=True)
+    for step in range(7):
+        if step == 3:
+            base[:] = 0
+        elif step == 4:
+            base[:] = N
+        elif step > 0:
+            base = np.clip(base + rng.integers(-300, 130, size=B), 0, N)
+        lens = np.stack([np.clip(base - 5 * (T - 1 - j) + rng.integers(-2, 3, size=B), -3, N + 3)
+                         for j in range(T)], axis=1).astype(np.int32)
+        say(f"score mtp incremental T={T} step {step}")
+        ld = torch.from_numpy(lens).cuda()
+        fresh = torch.full((B, T, N), float("nan"), dtype=torch.float32, device="cuda")
+        lib.score_mtp(q, w, t["k_pool"], t["page_table"], ld, out=fresh)
+        lib.score_mtp(q, w, t["k_pool"], t["page_table"], ld, out=kept, row_hwm=hwm)
+        torch.cuda.synchronize()
+        assert np.array_equal(kept.cpu().numpy().view(np.uint32), fresh.cpu().numpy().view(np.uint32)), step
+        assert np.array_equal(hwm.cpu().numpy(), np.clip(lens, 0, N).max(axis=1)), step
+        if step == 0:  # one step against the oracle too
+            check_mtp(fresh.cpu().numpy(), inp, wl.MtpInputs(mt.q_bits, mt.w, lens))
