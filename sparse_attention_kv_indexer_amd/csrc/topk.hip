@@ -16,40 +16,44 @@
 // before it) positions are taken, so counting those two kinds of keys in
 // position order places every chosen position.
 //
-// Two kernels, so that no workgroup ever waits on another one:
-//  * Segment kernel (rows longer than kSeg positions only; grid: requests x
+// One 1024-lane workgroup per request (the row kernel) selects its row's top
+// k. Every row of at most kSeg positions is its own candidate set, read
+// straight from the logits. A longer row is cut to candidates first: the keys
+// at or above a cut, with their positions, in position order in LDS. The
+// exact radix select then runs over the candidates at or above the cut only,
+// on digits of their offset from it (a narrow key range, so the first pass
+// spreads over many bins). If T lies below the cut (fewer than k keys reach
+// it) or more than kCap candidates remain, the workgroup selects over the
+// whole row instead, re-reading it from memory, so a cut never changes the
+// result. Where the cut and the candidates come from depends on the row
+// width:
+//  * Row width at most kRes (one kernel, no workspace): the workgroup loads
+//    the whole row into registers, cuts it at a key sampled from 64 runs of
+//    32 positions (loaded first, so the cut is picked while the row arrives),
+//    and stores the kept keys to LDS itself (gather_resident).
+//  * Wider rows (two kernels, so that no workgroup waits on another one): a
+//    segment kernel (rows longer than kSeg positions only; grid: requests x
 //    at most kSegGridY (8), 256 lanes, each workgroup taking every
-//    kSegGridY-th segment). A row is cut into segments of kSeg positions, so a
-//    long row is read by many compute units at once; lane t of a segment's
-//    workgroup holds the 16 consecutive positions at 16 t in registers. Two
-//    sampled keys per lane are counted into a histogram of the first digit,
-//    and the lower edge of the bin holding a generous estimate of the
-//    segment's share of the top k becomes its cut. Each wave writes its keys
-//    >= cut with their positions, in position order, to its own sub-slot of
-//    the workspace (so no scan spans the workgroup), and records its count.
-//  * Row kernel (one 1024-lane workgroup per request, so that many loads are
-//    in flight for the one compute unit). A row of at most kSeg positions is
-//    its own candidate set, read straight from the logits. A longer row
-//    gathers the sub-slots into LDS in order, hence position order: the first
-//    kSpec pairs of the first kSpecSlots sub-slots are loaded with 16-byte
-//    loads together with the counts, before the counts are known. If T is
-//    at or above every segment's cut, each key a segment left out is below T,
-//    so the candidates hold the whole top k and the chosen positions are
-//    written from them; hence the exact radix select runs over the
-//    candidates at or above the largest cut only, on digits of their offset
-//    from it (a narrow key range, so the first pass spreads over many bins).
-//    Otherwise (fewer than k keys at or above the largest cut, or more than
-//    kCap candidates) the workgroup selects over the whole row instead,
-//    re-reading it from memory.
+//    kSegGridY-th segment) cuts each segment of kSeg positions at the lower
+//    edge of the bin holding a generous estimate of the segment's share of
+//    the top k (from two sampled keys per lane), and each wave writes its
+//    kept keys with their positions, in position order, to its own sub-slot
+//    of the workspace, with its count. The row kernel gathers the sub-slots
+//    into LDS in order, hence position order (the first kSpec pairs of the
+//    first kSpecSlots sub-slots are loaded together with the counts, before
+//    the counts are known); the largest segment cut serves as the cut: if T
+//    is at or above every segment's cut, each key a segment left out is below
+//    T.
 //
 // With the score kernel's first-digit histogram of the row (the fused pair),
-// every segment cuts at the exact lower edge of the bin holding the k-th
-// largest key, the row kernel starts its select at the second digit, and it
-// sets the histogram back to zero.
+// the cut is the exact lower edge of the bin holding the k-th largest key
+// (for every segment, or for the row held in registers), the row kernel
+// starts its select at the second digit, and it sets the histogram back to
+// zero.
 //
-// A radix pass counts into a histogram in LDS; one wave then reads the whole
-// histogram and finds the digit (in the segment kernel every wave does so
-// itself, which spares a broadcast).
+// A radix pass counts into a histogram in LDS; all 16 waves of the row
+// kernel then pick the digit together (block_pick; in the segment kernel
+// every wave reads the whole histogram itself, which spares a broadcast).
 #include "common.h"
 
 namespace dsa {
