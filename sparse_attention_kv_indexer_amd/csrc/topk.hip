@@ -51,9 +51,9 @@
 // starts its select at the second digit, and it sets the histogram back to
 // zero.
 //
-// A radix pass counts into a histogram in LDS; all 16 waves of the row
-// kernel then pick the digit together (block_pick; in the segment kernel
-// every wave reads the whole histogram itself, which spares a broadcast).
+// A radix pass counts into a histogram in LDS; four waves of the row kernel,
+// one per SIMD, then pick the digit (block_pick; in the segment kernel every
+// wave reads the whole histogram itself, which spares a broadcast).
 #include "common.h"
 
 namespace dsa {
@@ -461,51 +461,74 @@ __device__ __forceinline__ void clear_hists() {
 }
 
 // The row kernel's pick over a histogram of kNB bins in LDS (complete, after
-// a barrier), shared by all its waves: lane t holds the kNB / 1024 bins just
-// below the top kNB / 1024 * t, each wave scans its lanes' counts, the wave
-// totals go through LDS, and the one lane whose bins hold the rank-th largest
-// counted key (rank = rank_of(total counted)) writes rs.bcast = {bin, keys in
-// higher bins, keys in the bin} ({0, total, 0} if rank exceeds the total).
-// Every lane must call it; it ends with a barrier, after which rs.bcast is
-// read. (Wave 0 alone reading all bins took about 0.75 us per pass.)
+// a barrier): waves 0-3, one per SIMD, read the bins, kNB / 256 per lane (lane
+// t the ones just below the top kNB / 256 * t), each scans its lanes' counts,
+// the four wave totals go through LDS, and the one lane whose bins hold the
+// rank-th largest counted key (rank = rank_of(total counted)) writes
+// rs.bcast = {bin, keys in higher bins, keys in the bin} ({0, total, 0} if
+// rank exceeds the total). The other waves only pass the barriers: a SIMD
+// runs its waves one after another, so a pick spread over all 16 waves took
+// four waves' worth of instructions per SIMD (about 0.6 us, and wave 0 alone
+// over 32 bins per lane 0.75 us). Every lane must call it; it ends with a
+// barrier, after which rs.bcast is read.
 template <int kNB, typename RankOf>
 __device__ __forceinline__ void block_pick(const uint32_t* h, RankOf rank_of) {
-  constexpr int kPer = kNB / kRowThreads;
-  static_assert(kPer == 1 || kPer == 2, "one or two bins per lane");
+  constexpr int kPickWaves = 4;
+  constexpr int kPer = kNB / (64 * kPickWaves);
+  static_assert(kPer == 4 || kPer == 8, "four or eight bins per lane");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const uint32_t hi = (uint32_t)(kNB - 1 - kPer * tid);  // this lane's higher bin
-  uint32_t c_hi, c_lo = 0u;
-  if constexpr (kPer == 2) {
-    // bins hi - 1 (even) and hi share a 4-bin chunk, which hslot keeps in order
-    const u32x2 v = *reinterpret_cast<const u32x2*>(h + hslot(hi - 1));
-    c_lo = v.x;
-    c_hi = v.y;
-  } else {
-    c_hi = h[hslot(hi)];
-  }
-  const uint32_t c = c_hi + c_lo;
-  const uint32_t incl = wave_inclusive_scan(c);
-  if (lane == 63) rs.part[wave] = incl;
-  __syncthreads();
-  uint32_t pre = 0u, total = 0u;
+  const bool picker = wave < kPickWaves;
+  const uint32_t lo = (uint32_t)(kNB - kPer * (min(tid, 64 * kPickWaves - 1) + 1));  // this lane's lowest bin
+  uint32_t c[kPer];
+  uint32_t sum = 0u, incl = 0u;
+  if (picker) {
 #pragma unroll
-  for (int w = 0; w < kRowWaves; ++w) {
-    const uint32_t t = rs.part[w];
-    pre += w < wave ? t : 0u;
-    total += t;
+    for (int q = 0; q < kPer / 4; ++q) {
+      // bins lo + 4q .. + 3: one 4-bin chunk, which hslot keeps in order
+      const u32x4 v = *reinterpret_cast<const u32x4*>(h + hslot(lo + 4 * q));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t x = v[e];
+        c[4 * q + e] = x;
+        sum += x;
+      }
+    }
+    incl = wave_inclusive_scan(sum);
+    if (lane == 63) rs.part[wave] = incl;
   }
-  const uint32_t rank = rank_of(total);
-  const uint32_t excl = pre + incl - c;
-  if (excl < rank && rank <= excl + c) {  // exactly one lane
-    const bool upper = rank <= excl + c_hi;
-    rs.bcast[0] = upper ? hi : hi - 1u;
-    rs.bcast[1] = upper ? excl : excl + c_hi;
-    rs.bcast[2] = upper ? c_hi : c_lo;
-  }
-  if (tid == 0 && rank > total) {
-    rs.bcast[0] = 0u;
-    rs.bcast[1] = total;
-    rs.bcast[2] = 0u;
+  __syncthreads();
+  if (picker) {
+    uint32_t pre = 0u, total = 0u;
+#pragma unroll
+    for (int w = 0; w < kPickWaves; ++w) {
+      const uint32_t t = rs.part[w];
+      pre += w < wave ? t : 0u;
+      total += t;
+    }
+    const uint32_t rank = rank_of(total);
+    const uint32_t excl = pre + incl - sum;
+    if (excl < rank && rank <= excl + sum) {  // exactly one lane: its bins, highest first
+      uint32_t acc = excl, bin = lo, above = excl, cnt = 0u;
+      bool done = false;
+#pragma unroll
+      for (int e = kPer - 1; e >= 0; --e) {
+        if (!done && acc + c[e] >= rank) {
+          bin = lo + (uint32_t)e;
+          above = acc;
+          cnt = c[e];
+          done = true;
+        }
+        acc += c[e];
+      }
+      rs.bcast[0] = bin;
+      rs.bcast[1] = above;
+      rs.bcast[2] = cnt;
+    }
+    if (tid == 0 && rank > total) {
+      rs.bcast[0] = 0u;
+      rs.bcast[1] = total;
+      rs.bcast[2] = 0u;
+    }
   }
   __syncthreads();
 }
