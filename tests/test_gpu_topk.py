@@ -293,9 +293,9 @@ def test_resident_rows_ties_zeros_nan_inf(lib):
     assert idx[5].tolist() == list(range(k))
 
 
-@pytest.mark.parametrize("k", [15356, 16000, 32767])
+@pytest.mark.parametrize("k", [15296, 16000, 32767])
 def test_resident_rows_with_k_past_the_candidate_capacity(lib, k):
-    """k at and past what a row workgroup holds in LDS (15,356 candidates):
+    """k at and past what a row workgroup holds in LDS (15,296 candidates):
     the rows are selected over whole, at a row width held in registers, next
     to a row of exactly k + 1 positions and one shorter than k."""
     rng = np.random.default_rng(k)
