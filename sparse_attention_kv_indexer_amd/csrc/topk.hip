@@ -709,7 +709,7 @@ __device__ __forceinline__ Kth select_candidates_ranged(int n, int k, uint32_t b
 
 // Writes the chosen positions from the n candidates in LDS (position order);
 // each lane takes a run of consecutive candidates.
-__device__ __forceinline__ void write_from_candidates(int n, Kth t, rsrc_t oi, rsrc_t ov, bool with_vals) {
+__device__ __forceinline__ void write_from_candidates(int n, Kth t, rsrc_t oi, rsrc_t ov, bool with_vals, bool raw) {
   const int tid = threadIdx.x;
   const int per = (n + kRowThreads - 1) / kRowThreads;  // <= kCap / kRowThreads
   const int c0 = min(tid * per, n), c1 = min(c0 + per, n);
@@ -728,7 +728,7 @@ __device__ __forceinline__ void write_from_candidates(int n, Kth t, rsrc_t oi, r
     const uint32_t kk = rs.cand_key[i];
     if (kk > t.T || (kk == t.T && eq_rank < t.r)) {
       store_b32(oi, (int)pos, rs.cand_pos[i]);
-      if (with_vals) store_b32(ov, (int)pos, key_to_bits(kk));
+      if (with_vals) store_b32(ov, (int)pos, raw ? kk : key_to_bits(kk));
       ++pos;
     }
     eq_rank += kk == t.T ? 1u : 0u;
@@ -945,9 +945,11 @@ __device__ __forceinline__ void block_scan_n(uint32_t (&v)[kN], uint32_t (&tot)[
 //
 // Writing the candidates: every lane stores every key it holds, a kept one at
 // its place in position order and any other one in the lane's spare slot
-// past kCap, so the stores need no branch; the keys are stored as the raw
-// score bits and turned into keys afterwards, over the candidates only.
-__device__ __forceinline__ int gather_resident(const float* row_ptr, int len, int k, bool hint) {
+// past kCap, so the stores need no branch. The values stored are the raw
+// score bits; with a cut above +0 they stay so (raw is set: the select then
+// works on raw bits, see below), otherwise one pass over the candidates turns
+// them into keys.
+__device__ __forceinline__ int gather_resident(const float* row_ptr, int len, int k, bool hint, bool& raw) {
   const int tid = threadIdx.x;
   const int n_blk = (len + kSeg - 1) / kSeg;  // 2 .. kResBlk
   // only positions [0, len) are readable through r1: a 16-byte load reaching
@@ -1045,19 +1047,35 @@ __device__ __forceinline__ int gather_resident(const float* row_ptr, int len, in
       }
     }
   }
-  __syncthreads();
-  // the candidates' keys, and the largest of them
+  // A cut above +0 keeps only positive floats and +inf, whose raw bits are
+  // ordered as their keys are (and differ from them by the top bit only): the
+  // candidates then stay raw bits, the select and its check run on raw bits,
+  // and the bound on the largest candidate is the largest of the held bits
+  // as signed integers (negative scores are negative, zeros past len are 0,
+  // a NaN only loosens the bound).
+  raw = !hint && lo > 0x80000000u;  // workgroup-uniform
   uint32_t mx = 0u;
-  for (int i = tid; i < (int)n; i += kRowThreads) {
-    const uint32_t kk = order_key(__uint_as_float(rs.cand_key[i]));
-    rs.cand_key[i] = kk;
-    mx = max(mx, kk);
+  if (raw) {
+    int im = 0;
+#pragma unroll
+    for (int j = 0; j < kResBlk; ++j)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) im = max(im, (int)v[j][e]);
+    mx = (uint32_t)im;
+  } else {
+    __syncthreads();
+    // the candidates' keys, and the largest of them
+    for (int i = tid; i < (int)n; i += kRowThreads) {
+      const uint32_t kk = order_key(__uint_as_float(rs.cand_key[i]));
+      rs.cand_key[i] = kk;
+      mx = max(mx, kk);
+    }
   }
   mx = wave_max(mx);
   if ((tid & 63) == 0) atomicMax(&rs.range[1], mx);
   if (tid == 0) {
     rs.range[0] = n;
-    rs.max_cut = lo;
+    rs.max_cut = raw ? (lo & 0x7FFFFFFFu) : lo;
   }
   return (int)n;
 }
@@ -1104,6 +1122,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
   }
   clear_hists();
   int n;
+  bool raw = false;  // candidates held as raw score bits (gather_resident)
   if (len <= kSeg) {
     // the row is its own candidate set
     uint32_t bits[kSeg / kRowThreads];
@@ -1119,7 +1138,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     }
     n = len;
   } else if (max_c4 <= kRes) {
-    n = gather_resident(row_ptr, len, k, hist != nullptr);
+    n = gather_resident(row_ptr, len, k, hist != nullptr, raw);
   } else {
     n = gather_segments(ws, b, (int)gridDim.x, n_seg, len);
   }
@@ -1153,7 +1172,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
                                              : select_candidates(n, k, from_hist, bin0, above0);
     // every key a segment left out lies below its cut, hence below T
     if (t.r != 0xFFFFFFFFu && t.T >= rs.max_cut) {
-      write_from_candidates(n, t, oi, ov, with_vals);
+      write_from_candidates(n, t, oi, ov, with_vals, raw);
       return;
     }
     __syncthreads();  // every wave is done with the histograms

@@ -293,6 +293,49 @@ def test_resident_rows_ties_zeros_nan_inf(lib):
     assert idx[5].tolist() == list(range(k))
 
 
+@pytest.mark.parametrize("width", [20000, 32768])
+def test_resident_rows_cut_near_zero_and_denormal(lib, width):
+    """Rows held in registers whose sampled cut lies just above +0, in the
+    positive denormals, or at or below zero, where the candidates are kept as
+    raw score bits only for a cut above +0: denormal k-th keys, the smallest
+    positive float tied, +inf and NaN beside positive candidates, +0 and -0
+    below a positive cut, and keys spanning every positive exponent. The
+    values must come back with the scores' own bits."""
+    rng = np.random.default_rng(23)
+    B, k = 10, 1500
+    x = rng.standard_normal((B, width)).astype(np.float32)
+    den = lambda n: rng.integers(1, 1 << 23, size=n, dtype=np.uint32).view(np.float32)
+    x[0] = -np.abs(x[0])
+    x[0, ::4] = den(len(x[0, ::4]))  # a quarter positive denormals: the cut is one of them
+    x[1] = -np.abs(x[1])
+    x[1, ::20] = np.abs(x[1, ::20])  # fewer than k positives: the k-th key is negative
+    x[2, ::9] = np.inf  # more +inf than k
+    x[3, ::7] = np.nan
+    x[3, 1::7] = -np.nan
+    x[4] = 0.0
+    x[4, ::2] = -0.0
+    x[4, ::10] = np.abs(x[4, ::10]) + 1e-30  # positives above a sea of zeros
+    x[5] = -1.0
+    x[5, ::3] = np.array([1], dtype=np.uint32).view(np.float32)[0]  # smallest positive float, tied
+    x[5, :500] = 2.0
+    bits = rng.integers(1, 0x7F800000, size=width, dtype=np.uint32)
+    x[6] = bits.view(np.float32)  # every positive exponent, denormals to the largest finite
+    x[6, 777] = np.inf
+    x[7] = 0.0  # all +0: the cut is at +0, not above it
+    x[7, 3::11] = 5.0
+    x[8] = np.abs(x[8]) * 1e-40  # mostly denormal, a few flushed to +0
+    x[9] = rng.standard_normal(width).astype(np.float32) - 3.0  # mostly negative, cut below zero
+    lens = np.array([width, width - 1, width, width - 3, width, width - 9, width, width, width - 2, width])
+    say(f"topk resident rows: cut near zero and in the denormals, width {width}")
+    xd, ld = _upload(x, lens)
+    idx, vals = run_topk(lib, xd, ld, k)
+    check_topk_exact(idx, vals, x, lens, k)
+    for b in range(B):
+        src = x[b, idx[b]]
+        fin = np.isfinite(src) & (src != 0)
+        assert np.array_equal(vals[b][fin].view(np.uint32), src[fin].view(np.uint32)), f"row {b}: value bits"
+
+
 @pytest.mark.parametrize("k", [15296, 16000, 32767])
 def test_resident_rows_with_k_past_the_candidate_capacity(lib, k):
     """k at and past what a row workgroup holds in LDS (15,296 candidates):
