@@ -76,6 +76,7 @@ constexpr int kRecWords = 8;                  // per segment: kept count of each
 
 constexpr int kRowThreads = 1024;             // row kernel
 constexpr int kRowWaves = kRowThreads / 64;
+static_assert(kRowWaves == 16, "wave_partials: one wave's totals per lane of a 16-lane DPP row");
 // LDS words of cand_key and of cand_pos each: 16320 puts cand_pos[i]
 // exactly 255 x 256 bytes past cand_key[i], so that one ds_write2st64_b32
 // stores a key and its position from one address (two separate stores cost
@@ -156,33 +157,53 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
 }
 
-// Inclusive scans of a and b over the workgroup's lanes in lane order, and
-// their totals; `part` is 2 * kWaves words of LDS. Every lane must call it;
-// it ends with a barrier, after which part may be rewritten.
-template <int kWaves>
+// The second half of a block scan over the 16 waves of a row workgroup: wave
+// w's kN (<= 4) wave totals sit at part[4w .. 4w + kN - 1], 16-byte aligned
+// (written by its lane 63, then a barrier). Every lane gets, for each q, the
+// sum over the waves before its own and the sum over all: each 16-lane row
+// of the wave takes one wave's totals per lane, scans them along the row
+// (DPP row shifts), and the two sums are read from lanes wave - 1 and 15.
+// (Each wave adding all 16 waves' totals itself took about 100 instructions
+// per wave for four values, where this takes about 30.)
+template <int kN>
+__device__ __forceinline__ void wave_partials(const uint32_t* part, uint32_t (&before)[kN], uint32_t (&all)[kN]) {
+  static_assert(kN <= 4, "four values per wave");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // 0 .. 15
+  const u32x4 p = *reinterpret_cast<const u32x4*>(part + 4 * (lane & 15));
+#pragma unroll
+  for (int q = 0; q < kN; ++q) {
+    uint32_t v = p[q];
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xF, 0xF, false);  // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xF, 0xF, false);  // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xF, 0xF, false);  // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xF, 0xF, false);  // row_shr:8
+    const uint32_t prev = (uint32_t)__builtin_amdgcn_readlane((int)v, max(wave - 1, 0));
+    before[q] = wave > 0 ? prev : 0u;
+    all[q] = (uint32_t)__builtin_amdgcn_readlane((int)v, 15);
+  }
+}
+
+// Inclusive scans of a and b over the row workgroup's lanes in lane order,
+// and their totals; `part` is 4 * 16 words of LDS, 16-byte aligned. Every
+// lane must call it; it ends with a barrier, after which part may be
+// rewritten.
 __device__ __forceinline__ void block_scan2(uint32_t& a, uint32_t& b, uint32_t* part, uint32_t* tot_a, uint32_t* tot_b) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   a = wave_inclusive_scan(a);
   b = wave_inclusive_scan(b);
   if (lane == 63) {
-    part[wave] = a;
-    part[kWaves + wave] = b;
+    part[4 * wave] = a;
+    part[4 * wave + 1] = b;
   }
   __syncthreads();
-  uint32_t add_a = 0, add_b = 0, all_a = 0, all_b = 0;
-#pragma unroll
-  for (int wv = 0; wv < kWaves; ++wv) {
-    const uint32_t pa = part[wv], pb = part[kWaves + wv];
-    add_a += wv < wave ? pa : 0u;
-    add_b += wv < wave ? pb : 0u;
-    all_a += pa;
-    all_b += pb;
-  }
+  uint32_t before[2], all[2];
+  wave_partials<2>(part, before, all);
   __syncthreads();
-  a += add_a;
-  b += add_b;
-  *tot_a = all_a;
-  *tot_b = all_b;
+  a += before[0];
+  b += before[1];
+  *tot_a = all[0];
+  *tot_b = all[1];
 }
 
 // From a histogram of kNB bins in LDS (complete, after a barrier), the bin
@@ -432,7 +453,7 @@ struct RowShared {
   uint32_t cnt[kRound];   // per sub-slot of a gather round: kept count
   uint32_t off[kRound];   //   its first candidate
   uint32_t roff[kRound];  //   its first pair not read ahead, in the round's list of those
-  uint32_t part[4 * kRowWaves];
+  __attribute__((aligned(16))) uint32_t part[4 * kRowWaves];  // four values per wave (wave_partials)
   uint32_t bcast[3];
   uint32_t hpick[3];  // from the score kernel's histogram: bin of the k-th largest, count above it, found
   uint32_t small[kSmall];  // the keys of the last bin, once at most kSmall remain
@@ -721,7 +742,7 @@ __device__ __forceinline__ void write_from_candidates(int n, Kth t, rsrc_t oi, r
   }
   const uint32_t my_gt = n_gt, my_eq = n_eq;
   uint32_t tot_gt, tot_eq;
-  block_scan2<kRowWaves>(n_gt, n_eq, rs.part, &tot_gt, &tot_eq);
+  block_scan2(n_gt, n_eq, rs.part, &tot_gt, &tot_eq);
   uint32_t eq_rank = n_eq - my_eq;
   uint32_t pos = (n_gt - my_gt) + min(t.r, eq_rank);
   for (int i = c0; i < c1; ++i) {
@@ -771,7 +792,7 @@ __device__ __noinline__ void select_whole_row(rsrc_t row, int len, int k, rsrc_t
     }
     const uint32_t my_gt = n_gt, my_eq = n_eq;
     uint32_t tot_gt, tot_eq;
-    block_scan2<kRowWaves>(n_gt, n_eq, rs.part, &tot_gt, &tot_eq);
+    block_scan2(n_gt, n_eq, rs.part, &tot_gt, &tot_eq);
     uint32_t eq_rank = eq_seen + n_eq - my_eq;
     uint32_t pos = gt_seen + (n_gt - my_gt) + min(remaining, eq_rank);
 #pragma unroll
@@ -823,7 +844,7 @@ __device__ __forceinline__ int gather_segments(const uint32_t* __restrict__ ws, 
     // pairs not read ahead
     const uint32_t rest = (u < n_spec) ? (cnt > (uint32_t)kSpec ? cnt - kSpec : 0u) : cnt;
     uint32_t incl = cnt, rincl = rest, tot, rtot;
-    block_scan2<kRowWaves>(incl, rincl, rs.part, &tot, &rtot);  // (its barriers also order max_cut's clearing)
+    block_scan2(incl, rincl, rs.part, &tot, &rtot);  // (its barriers also order max_cut's clearing)
     if ((tid & 63) == 0) atomicMax(&rs.max_cut, m);
     if ((uint32_t)n + tot > (uint32_t)kCap) return -1;  // workgroup-uniform
     if (tid < kRound) {
@@ -895,27 +916,19 @@ __device__ __forceinline__ int gather_segments(const uint32_t* __restrict__ ws, 
 // barrier, after which rs.part may be rewritten.
 template <int kN>
 __device__ __forceinline__ void block_scan_n(uint32_t (&v)[kN], uint32_t (&tot)[kN]) {
-  static_assert(kN * kRowWaves <= 4 * kRowWaves, "rs.part holds four values per wave");
+  static_assert(kN <= 4, "rs.part holds four values per wave");
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 #pragma unroll
   for (int q = 0; q < kN; ++q) v[q] = wave_inclusive_scan(v[q]);
   if (lane == 63) {
 #pragma unroll
-    for (int q = 0; q < kN; ++q) rs.part[q * kRowWaves + wave] = v[q];
+    for (int q = 0; q < kN; ++q) rs.part[4 * wave + q] = v[q];
   }
   __syncthreads();
+  uint32_t before[kN];
+  wave_partials<kN>(rs.part, before, tot);
 #pragma unroll
-  for (int q = 0; q < kN; ++q) {
-    uint32_t add = 0u, all = 0u;
-#pragma unroll
-    for (int w = 0; w < kRowWaves; ++w) {
-      const uint32_t p = rs.part[q * kRowWaves + w];
-      add += w < wave ? p : 0u;
-      all += p;
-    }
-    v[q] += add;
-    tot[q] = all;
-  }
+  for (int q = 0; q < kN; ++q) v[q] += before[q];
   __syncthreads();
 }
 
@@ -1160,7 +1173,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
       ab += d > bin0 ? 1u : 0u;
       ge += d >= bin0 ? 1u : 0u;
     }
-    block_scan2<kRowWaves>(ab, ge, rs.part, &tot_ab, &tot_ge);
+    block_scan2(ab, ge, rs.part, &tot_ab, &tot_ge);
     from_hist = tot_ab < (uint32_t)k && tot_ge >= (uint32_t)k;
     above0 = tot_ab;
   }
