@@ -14,7 +14,9 @@
 // number of keys == T that belong to the top k (the lowest positions first).
 // Before any point in position order, (keys > T before it) + min(r, keys == T
 // before it) positions are taken, so counting those two kinds of keys in
-// position order places every chosen position.
+// position order places every chosen position. (A row held in registers whose
+// cut lies above +0 keeps its candidates as the raw score bits instead: every
+// one is a positive float or +inf, whose bits order as the keys do.)
 //
 // One 1024-lane workgroup per request (the row kernel) selects its row's top
 // k. Every row of at most kSeg positions is its own candidate set, read
