@@ -1123,6 +1123,16 @@ __device__ __forceinline__ int gather_resident(const float* row_ptr, int len, in
   return (int)n;
 }
 
+// kWidth: the row width class, kNarrow (at most kSeg: every row is its own
+// candidate set), kResident (at most kRes: rows held in registers) or kWide
+// (the segment kernel ran); kHist: the score kernel's histogram is given.
+// Compiled apart, so that each launch runs code holding only its own paths:
+// the instruction cache is cold after a score launch (measured against one
+// kernel for all: top-k c3 12.2 -> 11.8 us, full 12.5 -> 12.1, c2 5.7 ->
+// 5.25, 64 rows of 128 positions 4.6 -> 4.2, the same at a 1M-token row
+// width 6.5 -> 6.1).
+enum { kNarrow = 0, kResident = 1, kWide = 2 };
+template <int kWidth, bool kHist>
 __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __restrict__ logits,
                                                                 const int32_t* __restrict__ seq_lens,
                                                                 int32_t max_c4, int32_t k,
@@ -1132,8 +1142,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
                                                                 uint32_t* __restrict__ hist) {
   const int b = blockIdx.x, tid = threadIdx.x;
   // this row's histogram, set back to zero for the next score call once read
-  const rsrc_t hrow = make_rsrc(hist != nullptr ? hist + (size_t)b * kHistBins : nullptr,
-                                hist != nullptr ? kHistBins * 4u : 0u);
+  const rsrc_t hrow = make_rsrc(kHist ? hist + (size_t)b * kHistBins : nullptr, kHist ? kHistBins * 4u : 0u);
   static_assert(kHistBins == 2 * kRowThreads, "two bins per lane");
   auto clear_hist_row = [&]() { store_pair(hrow, tid, 0u, 0u); };
   const int len = min(max(seq_lens[b], 0), max_c4);
@@ -1147,7 +1156,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
 
   if (len <= k) {
     // every valid position is chosen
-    if (hist != nullptr) clear_hist_row();
+    if (kHist) clear_hist_row();
     for (int i = tid; i < k; i += kRowThreads) {
       store_b32(oi, i, i < len ? (uint32_t)i : 0xFFFFFFFFu);
       if (with_vals) store_b32(ov, i, i < len ? load_b32(row, i) : 0x7FC00000u);
@@ -1155,7 +1164,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     return;
   }
 
-  if (hist != nullptr && tid < 64) {
+  if (kHist && tid < 64) {
     const Pick p = pick_row_hist(load_row_hist(hist, b), k);
     if (tid == 0) {
       rs.hpick[0] = p.bin;
@@ -1180,15 +1189,15 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
       }
     }
     n = len;
-  } else if (max_c4 <= kRes) {
-    n = gather_resident(row_ptr, len, k, hist != nullptr, raw);
-  } else {
+  } else if constexpr (kWidth == kResident) {
+    n = gather_resident(row_ptr, len, k, kHist, raw);
+  } else if constexpr (kWidth == kWide) {
     n = gather_segments(ws, b, (int)gridDim.x, n_seg, len);
   }
   __syncthreads();
-  bool from_hist = hist != nullptr && rs.hpick[2] != 0u;
+  bool from_hist = kHist && rs.hpick[2] != 0u;
   uint32_t bin0 = 0u, above0 = 0u;
-  if (hist != nullptr) clear_hist_row();  // wave 0 read it before the barrier
+  if (kHist) clear_hist_row();  // wave 0 read it before the barrier
   if (from_hist && n >= k) {
     // The histogram is taken only where the candidates confirm it: fewer than
     // k of them above its bin and at least k in or above it. The candidates
@@ -1211,8 +1220,13 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     // gathered candidates: the select over those at or above the largest cut
     // (with a histogram that the candidates did not confirm, the ranged select
     // over the candidates at or above the largest cut decides, as without one)
-    const Kth t = (!from_hist && len > kSeg) ? select_candidates_ranged(n, k, rs.max_cut, max_c4 <= kRes)
-                                             : select_candidates(n, k, from_hist, bin0, above0);
+    Kth t;
+    if constexpr (kWidth == kNarrow) {
+      t = select_candidates(n, k, from_hist, bin0, above0);
+    } else {
+      t = (!from_hist && len > kSeg) ? select_candidates_ranged(n, k, rs.max_cut, kWidth == kResident)
+                                     : select_candidates(n, k, from_hist, bin0, above0);
+    }
     // every key a segment left out lies below its cut, hence below T
     if (t.r != 0xFFFFFFFFu && t.T >= rs.max_cut) {
       write_from_candidates(n, t, oi, ov, with_vals, raw);
@@ -1243,8 +1257,20 @@ hipError_t launch_topk(const float* logits, const int32_t* seq_lens, int32_t bat
   if (max_c4 > kRes && k < max_c4)
     hipLaunchKernelGGL(topk_segment_kernel, dim3(batch, min(n_seg, kSegGridY)), dim3(kSegThreads), 0, stream, logits, seq_lens,
                        max_c4, k, n_seg, ws, hist);
-  hipLaunchKernelGGL(topk_row_kernel, dim3(batch), dim3(kRowThreads), 0, stream, logits, seq_lens, max_c4, k,
-                     out_idx, out_vals, ws, n_seg, hist);
+  const int width = max_c4 <= kSeg ? kNarrow : (max_c4 <= kRes ? kResident : kWide);
+#define DSA_ROW_LAUNCH(W, H)                                                                                   \
+  hipLaunchKernelGGL((topk_row_kernel<W, H>), dim3(batch), dim3(kRowThreads), 0, stream, logits, seq_lens, max_c4, \
+                     k, out_idx, out_vals, ws, n_seg, hist)
+  if (hist == nullptr) {
+    if (width == kNarrow) DSA_ROW_LAUNCH(kNarrow, false);
+    else if (width == kResident) DSA_ROW_LAUNCH(kResident, false);
+    else DSA_ROW_LAUNCH(kWide, false);
+  } else {
+    if (width == kNarrow) DSA_ROW_LAUNCH(kNarrow, true);
+    else if (width == kResident) DSA_ROW_LAUNCH(kResident, true);
+    else DSA_ROW_LAUNCH(kWide, true);
+  }
+#undef DSA_ROW_LAUNCH
   return hipGetLastError();
 }
 
