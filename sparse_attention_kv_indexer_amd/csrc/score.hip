@@ -245,13 +245,17 @@ void score_kernel(
 
   // bf16 keys: a page's 64 scores (per query token) go to an LDS stash,
   // written out as runs of contiguous logits at the end of the workgroup's
-  // pages (or when the stash is full) with 1 KiB streaming wave stores.
+  // pages (or when the stash is full) with 1 KiB wave stores.
   // Measured with a load probe over random 8 KiB pages: 256 B of results
   // stored after every page cost the read stream 6 us of 48 at 32768 pages;
   // the same bytes written in one burst per workgroup cost 2. (Measured in
   // the kernel: full 50.2 -> 48.4 us; two and three query tokens 1-2 us per
   // step faster; fp8 pages and four query tokens no gain, so they store per
-  // page. Streaming stores for the bursts: -0.3 to -0.5 us.)
+  // page.) Every logits store is written through the L2 (kWriteThrough):
+  // measured against streaming stores, the kernel alone is 0.3-0.4 us
+  // slower, but a score and top-k step is 0.5-0.7 us faster (B = 64 at 128K
+  // tokens; 0.3 us at B = 16 and 8K), since the kernel's end no longer
+  // writes the logits back from the L2s before the top-k can start.
   constexpr bool kStashed = !kFp8 && kTok <= 3;
   constexpr int kStash = kTok == 1 ? 32 : 8;  // pages; token t's rows at [t][page][64]
   __shared__ __attribute__((aligned(16))) uint32_t stash[kStashed ? kTok * kStash * kPage : 4];
@@ -274,7 +278,7 @@ void score_kernel(
                                      (uint32_t)words * 4u);
         for (int w0 = lane * 4; w0 < words; w0 += 256)
           __builtin_amdgcn_raw_buffer_store_b128(
-              *reinterpret_cast<const u32x4*>(&stash[(t * kStash + p) * kPage + w0]), out, w0 * 4, 0, kNonTemporal);
+              *reinterpret_cast<const u32x4*>(&stash[(t * kStash + p) * kPage + w0]), out, w0 * 4, 0, kWriteThrough);
       }
       p = q;
     }
@@ -450,7 +454,7 @@ void score_kernel(
           stash[(t * kStash + stash_n) * kPage + lane] = __builtin_bit_cast(uint32_t, v);
         } else {
           const rsrc_t out = make_rsrc(logits + ((int64_t)bx * kTok + t) * sh.width + base, kPage * sizeof(float));
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), out, lane * 4, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), out, lane * 4, 0, kWriteThrough);
         }
         if constexpr (kTok == 1 && !kFp8) {
           if (hist != nullptr) {
@@ -532,10 +536,8 @@ void score_kernel(
       for (int t = 0; t < kTok; ++t) {
         const rsrc_t row = make_rsrc(logits + ((int64_t)b * kTok + t) * sh.width, (uint32_t)sh.width * 4u);
         // c0 and c1 are multiples of 4 (page and row boundaries): whole 16-byte stores
-        // streaming stores: the tail is not read back soon (measured: faster where the tail dominates,
-        // unchanged elsewhere; the scored pages keep ordinary stores, which the top-k reads next)
         for (uint32_t p = c0 + 4 * lane; p < c1; p += 256)
-          __builtin_amdgcn_raw_buffer_store_b128(ninf, row, p * 4, 0, kNonTemporal);
+          __builtin_amdgcn_raw_buffer_store_b128(ninf, row, p * 4, 0, kWriteThrough);
       }
     }
   }
