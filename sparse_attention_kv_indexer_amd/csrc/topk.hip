@@ -25,14 +25,15 @@
 // exact radix select then runs over the candidates at or above the cut only,
 // on digits of their offset from it (a narrow key range, so the first pass
 // spreads over many bins). If T lies below the cut (fewer than k keys reach
-// it) or more than kCap candidates remain, the workgroup selects over the
-// whole row instead, re-reading it from memory, so a cut never changes the
-// result. Where the cut and the candidates come from depends on the row
+// it) or more candidates remain than LDS holds, the workgroup selects over
+// the whole row instead, re-reading it from memory, so a cut never changes
+// the result. Where the cut and the candidates come from depends on the row
 // width:
 //  * Row width at most kRes (one kernel, no workspace): the workgroup loads
 //    the whole row into registers, cuts it at a key sampled from 64 runs of
 //    32 positions (loaded first, so the cut is picked while the row arrives),
-//    and stores the kept keys to LDS itself (gather_resident).
+//    and each wave stores its chunk's kept keys to its own region of LDS as
+//    they arrive (gather_resident).
 //  * Wider rows (two kernels, so that no workgroup waits on another one): a
 //    segment kernel (rows longer than kSeg positions only; grid: requests x
 //    at most kSegGridY (8), 256 lanes, each workgroup taking every
@@ -84,7 +85,7 @@ static_assert(kRowWaves == 16, "wave_partials: one wave's totals per lane of a 1
 // stores a key and its position from one address (two separate stores cost
 // c3 top-k 13.91 vs 13.69 us, A/B on one box).
 constexpr int kSlots = 16320;
-constexpr int kCap = kSlots - kRowThreads;    // candidates a row workgroup holds in LDS (then one spare slot per lane)
+constexpr int kCap = kSlots - kRowThreads;    // candidates the row workgroup of the widest rows holds in LDS
 constexpr int kRound = 256;                   // sub-slot records per gather round
 constexpr int kSpecSlots = 32;                // sub-slots read before their counts are known
 constexpr int kSpec = 256;                    // pairs read ahead per such sub-slot
@@ -97,6 +98,12 @@ constexpr int kSmallRanged = 16;              // the same, in the ranged select 
 // kSamples keys in 64 runs of 32 consecutive positions spread over the row.
 constexpr int kRes = 32768;
 constexpr int kResBlk = kRes / kSeg;
+// In that kernel each wave keeps its candidates in a region of its own:
+// wave w's at slots [w kRegion, w kRegion + its count), so that it stores
+// them as its keys arrive, with no workgroup-wide scan.
+constexpr int kRegion = kSlots / kRowWaves;
+constexpr uint32_t kOverflow = 1u << 16;  // added to the candidate count for a region that overflowed
+static_assert(kRowWaves * kRegion + 3 * 64 <= 2 * kSlots, "the count's reads past a region stay in cand_pos");
 constexpr int kSamples = 2 * kRowThreads;     // the sample: 64 runs of 32 positions
 static_assert(kSeg == 4 * kRowThreads, "a block of kSeg positions is one 16-byte group per lane");
 static_assert(2 * kBins <= kCap, "the sample histograms fit in cand_pos");
@@ -471,6 +478,19 @@ __device__ __forceinline__ uint32_t* pass_hist(int pass) {
   return pass == 0 ? rs.hist0 : (pass == 1 ? rs.hist1 : rs.hist2);
 }
 
+// The candidate slots one lane visits, i = first, first + step, ... below
+// end, at rs.cand_key[base + i]: in the resident kernel (each wave's
+// candidates in its own region) the wave's lanes take its region, otherwise
+// the workgroup's lanes take [0, n).
+struct Slots {
+  int base, first, end, step;
+};
+__device__ __forceinline__ Slots all_slots(int n) { return Slots{0, (int)threadIdx.x, n, kRowThreads}; }
+__device__ __forceinline__ Slots region_slots(int count) {
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  return Slots{wave * kRegion, (int)(threadIdx.x & 63), count, 64};
+}
+
 // Clears the three histograms and max_cut (a barrier must follow before
 // they are counted into).
 __device__ __forceinline__ void clear_hists() {
@@ -587,12 +607,12 @@ __device__ __forceinline__ uint32_t radix_pass(uint32_t& T, uint32_t& mask, uint
 // 4096 positions: top-k 5.4 -> 5.0 us at 64 requests of 128 positions; on the
 // longer rows' ranged select it was slower, so that select keeps its passes.)
 template <typename Match>
-__device__ __forceinline__ void finish_small(int n, uint32_t remaining, Match match, uint32_t& T, uint32_t& r) {
+__device__ __forceinline__ void finish_small(const Slots& sl, uint32_t remaining, Match match, uint32_t& T, uint32_t& r) {
   const int tid = threadIdx.x;
   if (tid == 0) rs.small_n = 0u;
   __syncthreads();
-  for (int i = tid; i < n; i += kRowThreads) {
-    const uint32_t kk = rs.cand_key[i];
+  for (int i = sl.first; i < sl.end; i += sl.step) {
+    const uint32_t kk = rs.cand_key[sl.base + i];
     if (match(kk)) rs.small[atomicAdd(&rs.small_n, 1u)] = kk;  // exactly the bin's count, <= kSmall
   }
   __syncthreads();
@@ -648,23 +668,22 @@ __device__ __forceinline__ void finish_small(int n, uint32_t remaining, Match ma
 struct Kth {
   uint32_t T, r;
 };
-__device__ __forceinline__ Kth select_candidates(int n, int k, bool from_hist, uint32_t bin0, uint32_t above0) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ Kth select_candidates(const Slots& sl, int k, bool from_hist, uint32_t bin0, uint32_t above0) {
   uint32_t T = from_hist ? bin0 << 21 : 0u;
   uint32_t mask = from_hist ? 0xFFE00000u : 0u;
   uint32_t remaining = (uint32_t)k - (from_hist ? above0 : 0u);
   auto count = [&](uint32_t* h, int shift, uint32_t dmask) {
-    int i = tid;
-    for (; i + 3 * kRowThreads < n; i += 4 * kRowThreads) {
+    int i = sl.first;
+    for (; i + 3 * sl.step < sl.end; i += 4 * sl.step) {
       uint32_t kk[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) kk[u] = rs.cand_key[i + u * kRowThreads];
+      for (int u = 0; u < 4; ++u) kk[u] = rs.cand_key[sl.base + i + u * sl.step];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
         if ((kk[u] & mask) == T) atomicAdd(&h[hslot((kk[u] >> shift) & dmask)], 1u);
     }
-    for (; i < n; i += kRowThreads) {
-      const uint32_t kk = rs.cand_key[i];
+    for (; i < sl.end; i += sl.step) {
+      const uint32_t kk = rs.cand_key[sl.base + i];
       if ((kk & mask) == T) atomicAdd(&h[hslot((kk >> shift) & dmask)], 1u);
     }
   };
@@ -672,12 +691,12 @@ __device__ __forceinline__ Kth select_candidates(int n, int k, bool from_hist, u
   uint32_t r;
   if (!from_hist) {
     if (radix_pass<0>(T, mask, remaining, count) <= (uint32_t)kSmall) {
-      finish_small(n, remaining, in_bin, T, r);
+      finish_small(sl, remaining, in_bin, T, r);
       return Kth{T, r};
     }
   }
   if (radix_pass<1>(T, mask, remaining, count) <= (uint32_t)kSmall) {
-    finish_small(n, remaining, in_bin, T, r);
+    finish_small(sl, remaining, in_bin, T, r);
     return Kth{T, r};
   }
   radix_pass<2>(T, mask, remaining, count);
@@ -695,14 +714,15 @@ __device__ __forceinline__ Kth select_candidates(int n, int k, bool from_hist, u
 // selects over the whole row). Inline: as an out-of-line call it saved and
 // restored 40 registers per lane through scratch memory on every call (c3
 // top-k 14.56 -> 14.24 us inline). The histograms are clear on entry,
-// and rs.range is (0, 0), or with preset the count of candidates at or above
-// base and the largest key.
-__device__ __forceinline__ Kth select_candidates_ranged(int n, int k, uint32_t base, bool preset) {
+// and rs.range is (0, 0), or with preset every candidate is at or above base
+// and rs.range[1] is the largest key.
+__device__ __forceinline__ Kth select_candidates_ranged(const Slots& sl, int n, int k, uint32_t base, bool preset) {
   const int tid = threadIdx.x;
-  if (!preset) {  // (else the gather left rs.range set)
+  uint32_t n_above = (uint32_t)n;
+  if (!preset) {  // (else the gather left rs.range[1] set)
     uint32_t hi = 0u, above = 0u;
-    for (int i = tid; i < n; i += kRowThreads) {
-      const uint32_t kk = rs.cand_key[i];
+    for (int i = sl.first; i < sl.end; i += sl.step) {
+      const uint32_t kk = rs.cand_key[sl.base + i];
       hi = max(hi, kk);
       above += kk >= base ? 1u : 0u;
     }
@@ -713,8 +733,9 @@ __device__ __forceinline__ Kth select_candidates_ranged(int n, int k, uint32_t b
       atomicMax(&rs.range[1], hi);
     }
     __syncthreads();
+    n_above = rs.range[0];
   }
-  if (rs.range[0] < (uint32_t)k) return Kth{0u, 0xFFFFFFFFu};
+  if (n_above < (uint32_t)k) return Kth{0u, 0xFFFFFFFFu};
   const uint32_t span = rs.range[1] - base;
   int top = span == 0u ? 0 : 32 - __builtin_clz(span);  // bits of the offsets still to resolve
   uint32_t prefix = 0u, remaining = (uint32_t)k;
@@ -722,20 +743,21 @@ __device__ __forceinline__ Kth select_candidates_ranged(int n, int k, uint32_t b
     const int low = max(top - 11, 0), width = top - low;
     const uint32_t dmask = (1u << width) - 1u;
     uint32_t* h = pass_hist(pass);
-    // Four keys a lane per round, without branches: the reads may run past n
-    // (into cand_pos: n + 3 kRowThreads < 2 kSlots), and a key not counted
+    // Four keys a lane per round, without branches: the reads may run past
+    // the end (into cand_pos: n + 3 kRowThreads, and a region's end + 3 x 64,
+    // stay below 2 kSlots), and a key not counted
     // adds to the lane's own dummy word instead of a bin. (The same sweep on
     // the first 4 or 8 waves only, the others passing the barrier: c3 top-k
     // 12.21 -> 13.13 / 12.49 us. With fewer waves the LDS latency shows.)
-    for (int i = tid; i < n; i += 4 * kRowThreads) {
+    for (int i = sl.first; i < sl.end; i += 4 * sl.step) {
       uint32_t kk[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) kk[u] = rs.cand_key[i + u * kRowThreads];
+      for (int u = 0; u < 4; ++u) kk[u] = rs.cand_key[sl.base + i + u * sl.step];
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const uint32_t o = kk[u] - base;
         // o >> top in two shifts (top is 1 .. 32)
-        const bool c = (i + u * kRowThreads < n) & (kk[u] >= base) & (((o >> (top - 1)) >> 1) == prefix);
+        const bool c = (i + u * sl.step < sl.end) & (kk[u] >= base) & (((o >> (top - 1)) >> 1) == prefix);
         const uint32_t bin = hslot((o >> low) & dmask);
         atomicAdd(c ? &h[bin] : &rs.dummy[tid & 63], 1u);
       }
@@ -750,7 +772,7 @@ __device__ __forceinline__ Kth select_candidates_ranged(int n, int k, uint32_t b
     // (bcast is written again only after the next pass's first barrier)
     if (top > 0 && in_bin <= (uint32_t)kSmallRanged) {
       uint32_t T, r;
-      finish_small(n, remaining, [&](uint32_t kk) {
+      finish_small(sl, remaining, [&](uint32_t kk) {
         return kk >= base && (uint32_t)((uint64_t)(kk - base) >> top) == prefix; }, T, r);
       return Kth{T, r};
     }
@@ -758,12 +780,13 @@ __device__ __forceinline__ Kth select_candidates_ranged(int n, int k, uint32_t b
   return Kth{base + prefix, remaining};
 }
 
-// Writes the chosen positions from the n candidates in LDS (position order);
-// each lane takes a run of consecutive candidates.
-__device__ __forceinline__ void write_from_candidates(int n, Kth t, rsrc_t oi, rsrc_t ov, bool with_vals, bool raw) {
-  const int tid = threadIdx.x;
-  const int per = (n + kRowThreads - 1) / kRowThreads;  // <= kCap / kRowThreads
-  const int c0 = min(tid * per, n), c1 = min(c0 + per, n);
+// Writes the chosen positions from the n candidates in LDS (position order:
+// with kReg, region after region in wave order, each in position order);
+// each lane takes a run of consecutive candidates (of its wave's region).
+__device__ __forceinline__ void write_from_candidates(const Slots& sl, Kth t, rsrc_t oi, rsrc_t ov, bool with_vals, bool raw) {
+  const int m = sl.end, first = sl.first;  // candidates of the region (or the row), this lane's index among its lanes
+  const int per = (m + sl.step - 1) / sl.step;  // <= kCap / kRowThreads, or kRegion / 64
+  const int c0 = sl.base + min(first * per, m), c1 = sl.base + min(first * per + per, m);
   uint32_t n_gt = 0, n_eq = 0;
   for (int i = c0; i < c1; ++i) {
     const uint32_t kk = rs.cand_key[i];
@@ -964,14 +987,17 @@ __device__ __forceinline__ void block_scan_n(uint32_t (&v)[kN], uint32_t (&tot)[
 
 // The candidates of a row of kSeg < len <= kRes positions when the row width
 // is at most kRes (no segment kernel ran): the workgroup loads the whole row
-// into registers (lane t: positions 4t .. 4t + 3 of every block of kSeg), cuts
-// it, and writes the keys at or above the cut with their positions to LDS in
-// position order. Returns the candidate count, or -1 if more than kCap. Sets
-// rs.max_cut to the cut, which the select and its check then treat as the
-// largest segment cut: if the k-th largest key lies below it, the row takes
-// the whole-row select, so the cut never changes the result. Also sets
-// rs.range to (the count, the largest candidate key), which the ranged
-// select would otherwise sweep the candidates for.
+// into registers, each wave a contiguous chunk of it (C positions, a multiple
+// of 64, at most 2048; lane l holds chunk positions 256 j + 64 e + l), cuts
+// it, and each wave writes its keys at or above the cut with their positions
+// to its own region of LDS, in position order, as they arrive: the regions
+// in wave order are the candidates in position order. Returns the wave's
+// count; adds it to rs.range[0] (kOverflow for a region that overflowed),
+// which the caller reads after a barrier. Sets rs.max_cut to the cut, which
+// the select and its check then treat as the largest segment cut: if the
+// k-th largest key lies below it, the row takes the whole-row select, so the
+// cut never changes the result, and rs.range[1] to the largest candidate
+// key, which the ranged select would otherwise sweep the candidates for.
 //
 // The cut: with the score kernel's histogram (hint, and wave 0's pick of it
 // in rs.hpick), that pick's bin edge. Otherwise a sample of n_s = kSamples
@@ -986,17 +1012,21 @@ __device__ __forceinline__ void block_scan_n(uint32_t (&v)[kN], uint32_t (&tot)[
 // sample histograms live in rs.cand_pos, which the candidates overwrite
 // afterwards. The three radix histograms are untouched.
 //
-// Writing the candidates: every lane stores every key it holds, a kept one at
-// its place in position order and any other one in the lane's spare slot
-// past kCap, so the stores need no branch. The values stored are the raw
-// score bits; with a cut above +0 they stay so (raw is set: the select then
-// works on raw bits, see below), otherwise one pass over the candidates turns
-// them into keys.
+// Writing the candidates: for each of the 32 keys a lane holds (64
+// consecutive positions across the wave), the wave takes a ballot of the
+// kept ones and each kept key goes to the next free slot of the region in
+// lane order, so no scan over the workgroup is needed and no barrier comes
+// until all are stored, and a wave stores each block as it arrives. (Against
+// 16-byte loads of four positions per lane spread over the row, a
+// workgroup-wide scan of the kept counts and stores after the whole row had
+// arrived: c3 top-k 11.8 -> 11.4 us, full 12.1 -> 11.7.) The values stored
+// are the raw score bits; with a cut above +0 they stay so (raw is set: the
+// select then works on raw bits, see below), otherwise each wave turns its
+// own into keys.
 __device__ __forceinline__ int gather_resident(const float* row_ptr, int len, int k, bool hint, bool& raw) {
   const int tid = threadIdx.x;
-  const int n_blk = (len + kSeg - 1) / kSeg;  // 2 .. kResBlk
-  // only positions [0, len) are readable through r1: a 16-byte load reaching
-  // past len reads 0 for each word past it (the range is checked per word)
+  // only positions [0, len) are readable through r1: a load reaching past
+  // len reads 0 for each word past it (the range is checked per word)
   const rsrc_t r1 = make_rsrc(row_ptr, (uint32_t)len * 4u);
   // the sample first: 64 runs of 32 consecutive positions spread over the
   // row (two positions per lane), so the cut is picked while the row arrives
@@ -1010,9 +1040,18 @@ __device__ __forceinline__ int gather_resident(const float* row_ptr, int len, in
   // (the barrier does not wait for loads: every wave's sample load is issued
   // before any row load, so the samples come back first)
   __syncthreads();
-  u32x4 v[kResBlk];
+  // this wave's chunk of the row: c0 + [0, cl), C positions (a multiple of
+  // 64, at most 2048) per wave; lane l holds positions c0 + 256 j + 64 e + l
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int C = (len + 64 * kRowWaves - 1) / (64 * kRowWaves) * 64;
+  const int c0 = wave * C, cl = min(max(len - c0, 0), C), nb = (cl + 255) / 256;
+  const rsrc_t rc = make_rsrc(row_ptr + min(c0, len), (uint32_t)cl * 4u);  // reads past cl return 0
+  uint32_t v[kResBlk][4];
 #pragma unroll
-  for (int j = 0; j < kResBlk; ++j) v[j] = __builtin_amdgcn_raw_buffer_load_b128(r1, (j * kSeg + 4 * tid) * 4, 0, 0);
+  for (int j = 0; j < kResBlk; ++j)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[j][e] = __builtin_amdgcn_raw_buffer_load_b32(rc, (256 * j + 64 * e + lane) * 4, 0, 0);
 
   uint32_t lo;
   const uint32_t n_s = kSamples;
@@ -1043,84 +1082,103 @@ __device__ __forceinline__ int gather_resident(const float* row_ptr, int len, in
     lo = max(lo, 1u);
   }
 
-  // key >= lo <=> score >= the float of lo, except that NaN (key 1) passes
-  // only when lo is at or below -inf's key: then every valid key is kept
-  const bool keep_all = lo <= 0x007FFFFFu;
-  const float f = __uint_as_float(key_to_bits(lo));
-  auto kept = [&](int j, int e) -> bool {
-    return (keep_all || __uint_as_float(v[j][e]) >= f) && j * kSeg + 4 * tid + e < len;
-  };
-  uint32_t pk[kResBlk / 2];  // kept counts of blocks 2q and 2q + 1, 16 bits each
-#pragma unroll
-  for (int q = 0; q < kResBlk / 2; ++q) {
-    uint32_t c0 = 0u, c1 = 0u;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      c0 += kept(2 * q, e) ? 1u : 0u;
-      c1 += kept(2 * q + 1, e) ? 1u : 0u;
-    }
-    pk[q] = c0 | (c1 << 16);
-  }
-  uint32_t incl[kResBlk / 2], tot[kResBlk / 2];
-#pragma unroll
-  for (int q = 0; q < kResBlk / 2; ++q) incl[q] = pk[q];
-  block_scan_n<kResBlk / 2>(incl, tot);  // 16-bit fields: at most kSeg per block
-  uint32_t n = 0u, off[kResBlk];
+  // key >= lo <=> score >= the float of lo, except for NaN (key 1). With lo
+  // at or below -inf's key the test is score >= -inf, which leaves out NaN
+  // scores: they are the smallest keys, so they belong to the top k only if
+  // fewer than k other keys are valid, and then the candidates fall short of
+  // k and the whole-row select runs. Positions past the chunk (read as 0) of
+  // its last block are set to NaN first, so they fail the test.
+  const float f = lo <= 0x007FFFFFu ? -__builtin_inff() : __uint_as_float(key_to_bits(lo));
+  raw = !hint && lo > 0x80000000u;  // workgroup-uniform
+  char* const reg = reinterpret_cast<char*>(rs.cand_key + wave * kRegion);  // rs.cand_pos lies kSlots words further
+  uint32_t wo = 0u;  // the region's next free slot (wave-uniform)
+  bool over = false;
+  int im = 0;
 #pragma unroll
   for (int j = 0; j < kResBlk; ++j) {
-    const int sh = 16 * (j & 1);
-    off[j] = n + ((incl[j / 2] >> sh) & 0xFFFFu) - ((pk[j / 2] >> sh) & 0xFFFFu);
-    n += (tot[j / 2] >> sh) & 0xFFFFu;
-  }
-  if (n > (uint32_t)kCap) return -1;  // workgroup-uniform
-  // byte offsets into rs.cand_key (rs.cand_pos lies kSlots words further)
-  const uint32_t spare = 4u * (uint32_t)(kCap + tid);
-  char* const ck = reinterpret_cast<char*>(rs.cand_key);
+    if (j < nb && !over) {
+      // a block adds at most 256 keys to the region: with fewer slots left
+      // the row takes the whole-row select (far past any cut the sample sets
+      // for k up to a third of the row)
+      over = wo + 4 * 64 > (uint32_t)kRegion;
+      if (!over) {
+        if (256 * (j + 1) > cl) {
 #pragma unroll
-  for (int j = 0; j < kResBlk; ++j) {
-    if (j < n_blk) {
-      uint32_t o = 4u * off[j];
+          for (int e = 0; e < 4; ++e) v[j][e] = 256 * j + 64 * e + lane < cl ? v[j][e] : 0xFFC00000u;
+        }
+        // (raw: the largest held bits as signed integers, the largest score;
+        // negative scores and the NaN set above are negative)
+        if (raw) {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const bool c = kept(j, e);
-        uint32_t* at = reinterpret_cast<uint32_t*>(ck + (c ? o : spare));
-        at[0] = v[j][e];
-        at[kSlots] = (uint32_t)(j * kSeg + 4 * tid + e);  // rs.cand_pos
-        o += c ? 4u : 0u;
+          for (int e = 0; e < 4; ++e) im = max(im, (int)v[j][e]);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const bool c = __uint_as_float(v[j][e]) >= f;
+          const uint64_t m = __builtin_amdgcn_ballot_w64(c);
+          if (c) {
+            const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+            uint32_t* const at = reinterpret_cast<uint32_t*>(reg + 4u * wo + 4u * r);
+            at[0] = v[j][e];
+            at[kSlots] = (uint32_t)(c0 + lane + 256 * j + 64 * e);  // rs.cand_pos
+          }
+          wo += (uint32_t)__builtin_popcountll(m);
+        }
       }
     }
   }
-  // A cut above +0 keeps only positive floats and +inf, whose raw bits are
-  // ordered as their keys are (and differ from them by the top bit only): the
-  // candidates then stay raw bits, the select and its check run on raw bits,
-  // and the bound on the largest candidate is the largest of the held bits
-  // as signed integers (negative scores are negative, zeros past len are 0,
-  // a NaN only loosens the bound).
-  raw = !hint && lo > 0x80000000u;  // workgroup-uniform
-  uint32_t mx = 0u;
-  if (raw) {
-    int im = 0;
-#pragma unroll
-    for (int j = 0; j < kResBlk; ++j)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) im = max(im, (int)v[j][e]);
-    mx = (uint32_t)im;
-  } else {
-    __syncthreads();
-    // the candidates' keys, and the largest of them
-    for (int i = tid; i < (int)n; i += kRowThreads) {
-      const uint32_t kk = order_key(__uint_as_float(rs.cand_key[i]));
-      rs.cand_key[i] = kk;
+  // the largest candidate (A cut above +0 keeps only positive floats and
+  // +inf, whose raw bits are ordered as their keys are, and differ from them
+  // by the top bit only: the candidates then stay raw bits, and the select
+  // and its check run on raw bits; the largest score bounds them);
+  // otherwise the region's keys, turned into keys here
+  const int nw = over ? 0 : (int)wo;
+  uint32_t mx = (uint32_t)im;
+  if (!raw) {
+    uint32_t* const rk = reinterpret_cast<uint32_t*>(reg);
+    mx = 0u;
+    for (int i = lane; i < nw; i += 64) {
+      const uint32_t kk = order_key(__uint_as_float(rk[i]));
+      rk[i] = kk;
       mx = max(mx, kk);
     }
   }
   mx = wave_max(mx);
-  if ((tid & 63) == 0) atomicMax(&rs.range[1], mx);
-  if (tid == 0) {
-    rs.range[0] = n;
-    rs.max_cut = raw ? (lo & 0x7FFFFFFFu) : lo;
+  if (lane == 0) {
+    atomicAdd(&rs.range[0], over ? kOverflow : wo);
+    atomicMax(&rs.range[1], mx);
   }
-  return (int)n;
+  if (tid == 0) rs.max_cut = raw ? (lo & 0x7FFFFFFFu) : lo;
+  return nw;
+}
+
+// A row of at most kSeg positions in the regions' layout: lane t loads
+// positions 4t .. 4t + 3, and wave w's region holds the valid positions
+// 256 w + i at slot i, as keys. Adds the count to rs.range[0] and returns the
+// wave's; every valid key is a candidate.
+__device__ __forceinline__ int load_short_regions(const float* row_ptr, int len) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const u32x4 x = __builtin_amdgcn_raw_buffer_load_b128(make_rsrc(row_ptr, (uint32_t)len * 4u), 16 * tid, 0, 0);
+  uint32_t* const rk = rs.cand_key + wave * kRegion;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int p = 4 * tid + e;
+    if (p < len) {
+      rk[4 * lane + e] = order_key(__uint_as_float(x[e]));
+      rk[4 * lane + e + kSlots] = (uint32_t)p;  // rs.cand_pos
+    }
+  }
+  const int nw = min(max(len - 256 * wave, 0), 256);
+  if (lane == 0) atomicAdd(&rs.range[0], (uint32_t)nw);
+  return nw;
+}
+
+// After a barrier: the candidates of all regions (rs.range[0]), or -1 if a
+// region overflowed.
+__device__ __forceinline__ int region_total() {
+  const uint32_t t = rs.range[0];
+  return t >= kOverflow ? -1 : (int)t;
 }
 
 // kWidth: the row width class, kNarrow (at most kSeg: every row is its own
@@ -1173,28 +1231,37 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     }
   }
   clear_hists();
+  // the resident kernel keeps its candidates in per-wave regions
+  constexpr bool kReg = kWidth == kResident;
   int n;
+  int nw = 0;  // kReg: this wave's candidates
   bool raw = false;  // candidates held as raw score bits (gather_resident)
   if (len <= kSeg) {
     // the row is its own candidate set
-    uint32_t bits[kSeg / kRowThreads];
+    if constexpr (kReg) {
+      nw = load_short_regions(row_ptr, len);
+    } else {
+      uint32_t bits[kSeg / kRowThreads];
 #pragma unroll
-    for (int m = 0; m < kSeg / kRowThreads; ++m) bits[m] = load_b32(row, m * kRowThreads + tid);  // 0 past len
+      for (int m = 0; m < kSeg / kRowThreads; ++m) bits[m] = load_b32(row, m * kRowThreads + tid);  // 0 past len
 #pragma unroll
-    for (int m = 0; m < kSeg / kRowThreads; ++m) {
-      const int i = m * kRowThreads + tid;
-      if (i < len) {
-        rs.cand_key[i] = order_key(__uint_as_float(bits[m]));
-        rs.cand_pos[i] = (uint32_t)i;
+      for (int m = 0; m < kSeg / kRowThreads; ++m) {
+        const int i = m * kRowThreads + tid;
+        if (i < len) {
+          rs.cand_key[i] = order_key(__uint_as_float(bits[m]));
+          rs.cand_pos[i] = (uint32_t)i;
+        }
       }
+      n = len;
     }
-    n = len;
   } else if constexpr (kWidth == kResident) {
-    n = gather_resident(row_ptr, len, k, kHist, raw);
+    nw = gather_resident(row_ptr, len, k, kHist, raw);
   } else if constexpr (kWidth == kWide) {
     n = gather_segments(ws, b, (int)gridDim.x, n_seg, len);
   }
   __syncthreads();
+  if constexpr (kReg) n = region_total();
+  const Slots sl = kReg ? region_slots(nw) : all_slots(n);
   bool from_hist = kHist && rs.hpick[2] != 0u;
   uint32_t bin0 = 0u, above0 = 0u;
   if (kHist) clear_hist_row();  // wave 0 read it before the barrier
@@ -1207,8 +1274,8 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     // cannot change the result.
     bin0 = rs.hpick[0];
     uint32_t ab = 0u, ge = 0u, tot_ab, tot_ge;
-    for (int i = tid; i < n; i += kRowThreads) {
-      const uint32_t d = rs.cand_key[i] >> 21;
+    for (int i = sl.first; i < sl.end; i += sl.step) {
+      const uint32_t d = rs.cand_key[sl.base + i] >> 21;
       ab += d > bin0 ? 1u : 0u;
       ge += d >= bin0 ? 1u : 0u;
     }
@@ -1222,14 +1289,14 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     // over the candidates at or above the largest cut decides, as without one)
     Kth t;
     if constexpr (kWidth == kNarrow) {
-      t = select_candidates(n, k, from_hist, bin0, above0);
+      t = select_candidates(sl, k, from_hist, bin0, above0);
     } else {
-      t = (!from_hist && len > kSeg) ? select_candidates_ranged(n, k, rs.max_cut, kWidth == kResident)
-                                     : select_candidates(n, k, from_hist, bin0, above0);
+      t = (!from_hist && len > kSeg) ? select_candidates_ranged(sl, n, k, rs.max_cut, kReg)
+                                     : select_candidates(sl, k, from_hist, bin0, above0);
     }
     // every key a segment left out lies below its cut, hence below T
     if (t.r != 0xFFFFFFFFu && t.T >= rs.max_cut) {
-      write_from_candidates(n, t, oi, ov, with_vals, raw);
+      write_from_candidates(sl, t, oi, ov, with_vals, raw);
       return;
     }
     __syncthreads();  // every wave is done with the histograms
