@@ -1097,32 +1097,37 @@ __device__ __forceinline__ int gather_resident(const float* row_ptr, int len, in
 #pragma unroll
   for (int j = 0; j < kResBlk; ++j) {
     if (j < nb && !over) {
-      // a block adds at most 256 keys to the region: with fewer slots left
-      // the row takes the whole-row select (far past any cut the sample sets
-      // for k up to a third of the row)
-      over = wo + 4 * 64 > (uint32_t)kRegion;
+      if (256 * (j + 1) > cl) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[j][e] = 256 * j + 64 * e + lane < cl ? v[j][e] : 0xFFC00000u;
+      }
+      // (raw: the largest held bits as signed integers, the largest score;
+      // negative scores and the NaN set above are negative)
+      if (raw) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) im = max(im, (int)v[j][e]);
+      }
+      bool c[4];
+      uint64_t m[4];
+      uint32_t cnt = 0u;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        c[e] = __uint_as_float(v[j][e]) >= f;
+        m[e] = __builtin_amdgcn_ballot_w64(c[e]);
+        cnt += (uint32_t)__builtin_popcountll(m[e]);
+      }
+      over = wo + cnt > (uint32_t)kRegion;  // the row then takes the whole-row select
       if (!over) {
-        if (256 * (j + 1) > cl) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) v[j][e] = 256 * j + 64 * e + lane < cl ? v[j][e] : 0xFFC00000u;
-        }
-        // (raw: the largest held bits as signed integers, the largest score;
-        // negative scores and the NaN set above are negative)
-        if (raw) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) im = max(im, (int)v[j][e]);
-        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool c = __uint_as_float(v[j][e]) >= f;
-          const uint64_t m = __builtin_amdgcn_ballot_w64(c);
-          if (c) {
-            const uint32_t r = __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+          if (c[e]) {
+            const uint32_t r =
+                __builtin_amdgcn_mbcnt_hi((uint32_t)(m[e] >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m[e], 0u));
             uint32_t* const at = reinterpret_cast<uint32_t*>(reg + 4u * wo + 4u * r);
             at[0] = v[j][e];
             at[kSlots] = (uint32_t)(c0 + lane + 256 * j + 64 * e);  // rs.cand_pos
           }
-          wo += (uint32_t)__builtin_popcountll(m);
+          wo += (uint32_t)__builtin_popcountll(m[e]);
         }
       }
     }
@@ -1154,8 +1159,8 @@ __device__ __forceinline__ int gather_resident(const float* row_ptr, int len, in
 
 // A row of at most kSeg positions in the regions' layout: lane t loads
 // positions 4t .. 4t + 3, and wave w's region holds the valid positions
-// 256 w + i at slot i, as keys. Adds the count to rs.range[0] and returns the
-// wave's; every valid key is a candidate.
+// 256 w + i at slot i, as keys. Returns the wave's count; every valid key is
+// a candidate, so the row's is len.
 __device__ __forceinline__ int load_short_regions(const float* row_ptr, int len) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -1169,9 +1174,7 @@ __device__ __forceinline__ int load_short_regions(const float* row_ptr, int len)
       rk[4 * lane + e + kSlots] = (uint32_t)p;  // rs.cand_pos
     }
   }
-  const int nw = min(max(len - 256 * wave, 0), 256);
-  if (lane == 0) atomicAdd(&rs.range[0], (uint32_t)nw);
-  return nw;
+  return min(max(len - 256 * wave, 0), 256);
 }
 
 // After a barrier: the candidates of all regions (rs.range[0]), or -1 if a
@@ -1260,7 +1263,7 @@ __global__ __launch_bounds__(kRowThreads) void topk_row_kernel(const float* __re
     n = gather_segments(ws, b, (int)gridDim.x, n_seg, len);
   }
   __syncthreads();
-  if constexpr (kReg) n = region_total();
+  if constexpr (kReg) n = len <= kSeg ? len : region_total();
   const Slots sl = kReg ? region_slots(nw) : all_slots(n);
   bool from_hist = kHist && rs.hpick[2] != 0u;
   uint32_t bin0 = 0u, above0 = 0u;
