@@ -491,10 +491,11 @@ __device__ __forceinline__ Slots region_slots(int count) {
   return Slots{wave * kRegion, (int)(threadIdx.x & 63), count, 64};
 }
 
-// Clears the three histograms and max_cut (a barrier must follow before
-// they are counted into).
+// Clears the three histograms, max_cut and the last bin's key count (a
+// barrier must follow before they are counted into).
 __device__ __forceinline__ void clear_hists() {
   if (threadIdx.x == 0) {
+    rs.small_n = 0u;
     rs.max_cut = 0u;
     rs.range[0] = 0u;
     rs.range[1] = 0u;
@@ -604,13 +605,13 @@ __device__ __forceinline__ uint32_t radix_pass(uint32_t& T, uint32_t& mask, uint
 // top k), instead of the radix passes left: the keys of the bin are collected
 // in LDS and wave 0 ranks them, one per lane, against each other. match(key)
 // tells a key of the bin. Every lane must call it. (Measured on rows of at most
-// 4096 positions: top-k 5.4 -> 5.0 us at 64 requests of 128 positions; on the
-// longer rows' ranged select it was slower, so that select keeps its passes.)
+// 4096 positions: top-k 5.4 -> 5.0 us at 64 requests of 128 positions; the
+// ranged select over longer rows' candidates ends this way once at most
+// kSmallRanged keys remain.)
 template <typename Match>
 __device__ __forceinline__ void finish_small(const Slots& sl, uint32_t remaining, Match match, uint32_t& T, uint32_t& r) {
   const int tid = threadIdx.x;
-  if (tid == 0) rs.small_n = 0u;
-  __syncthreads();
+  // (rs.small_n is zero from clear_hists: a select finishes this way once)
   for (int i = sl.first; i < sl.end; i += sl.step) {
     const uint32_t kk = rs.cand_key[sl.base + i];
     if (match(kk)) rs.small[atomicAdd(&rs.small_n, 1u)] = kk;  // exactly the bin's count, <= kSmall
