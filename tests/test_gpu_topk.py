@@ -349,3 +349,30 @@ def test_resident_rows_with_k_past_the_candidate_capacity(lib, k):
     xd, ld = _upload(x, lens)
     idx, vals = run_topk(lib, xd, ld, k)
     check_topk_exact(idx, vals, x, lens, k)
+
+
+@pytest.mark.parametrize("width", [32768, SEGMENT_WIDTH])
+def test_top_scores_crowded_into_one_stretch(lib, width):
+    """The largest scores crowded into one stretch of positions (the last
+    2048, the first 2048, one run in the middle, every 16th block of 64):
+    rows held in registers keep each wave's candidates in a region for its own
+    contiguous share of the row, so a stretch that holds the whole top k
+    overflows one region and sends the row to the whole-row select; the result
+    must not change."""
+    rng = np.random.default_rng(7)
+    B, N = 8, 32768
+    k = 2048
+    x = rng.standard_normal((B, N)).astype(np.float32)
+    lens = np.array([32768, 32768, 30001, 20000, 32768, 9000, 32768, 16385])
+    hot = [(N - 2048, N), (0, 2048), (12000, 15000), None, (32768 - 4096, 32768 - 1024), (0, 3000),
+           (16384, 18432), (14000, 16385)]
+    for b, span in enumerate(hot):
+        if span is None:  # every 16th block of 64 positions
+            for s0 in range(0, N, 1024):
+                x[b, s0:s0 + 64] += 8.0
+        else:
+            x[b, span[0]:span[1]] += 8.0
+    say(f"topk crowded top scores width={width}")
+    xd, ld = _upload(_widen(x, width), lens)
+    idx, vals = run_topk(lib, xd, ld, k)
+    check_topk_exact(idx, vals, x, lens, k)
