@@ -1088,7 +1088,8 @@ __device__ __forceinline__ int gather_resident(const float* row_ptr, int len, in
   // scores: they are the smallest keys, so they belong to the top k only if
   // fewer than k other keys are valid, and then the candidates fall short of
   // k and the whole-row select runs. Positions past the chunk (read as 0) of
-  // its last block are set to NaN first, so they fail the test.
+  // its last block are set to a negative NaN first, so they fail the test
+  // and stay below the raw-bits maximum.
   const float f = lo <= 0x007FFFFFu ? -__builtin_inff() : __uint_as_float(key_to_bits(lo));
   raw = !hint && lo > 0x80000000u;  // workgroup-uniform
   char* const reg = reinterpret_cast<char*>(rs.cand_key + wave * kRegion);  // rs.cand_pos lies kSlots words further
