@@ -39,6 +39,12 @@ METRIC = "valid positions scored/s + µs/step at B=64,128K ctx; % of HBM rooflin
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.txt")
 SCORE_SOURCES = ["sparse_attention_kv_indexer_amd/csrc/score.hip", "sparse_attention_kv_indexer_amd/csrc/common.h"]
 BATCHES = 5  # timed batches; the launch averages are their median
+# Steps per captured graph (at least; a multiple of the input copies, taken in
+# turn): each replay of a graph is followed by a gap of a few microseconds on
+# the GPU before the next one starts, so a graph of only the R copies' steps
+# (two at c3) adds about 1 us to every step. A decode step's graph holds the
+# indexer of many layers.
+GRAPH_STEPS = 16
 
 
 def parse():
@@ -323,13 +329,14 @@ def cu_count() -> int:
 
 def measure_step(cfg_name: str, steps: int, warmup: int, hwm=False, keys="bf16", T=1, fused=False, rotate=0,
                  inp=None) -> dict:
-    """One workload: R input copies and one captured graph of R consecutive
-    steps [score; top-k], one per copy (as a decode step's graph holds the
-    indexer of consecutive layers, each over its own keys), `warmup` untimed
-    steps, then exactly `steps` timed steps in BATCHES batches (events between
-    batches, no synchronization), and the median per-launch duration of the
-    score and top-k calls alone. Also times one-step graphs, whose replay
-    overhead is reported beside the step."""
+    """One workload: R input copies and one captured graph of S consecutive
+    steps [score; top-k] (S >= GRAPH_STEPS, a multiple of R), the copies in
+    turn (as a decode step's graph holds the indexer of consecutive layers,
+    each over its own keys), `warmup` untimed steps (rounded up to whole
+    graphs), then exactly `steps` timed steps in BATCHES batches (events
+    between batches, no synchronization), and the median per-launch duration
+    of the score and top-k calls alone. Also times one-step graphs, whose
+    replay overhead is reported beside the step."""
     import numpy as np
     import torch
 
@@ -387,8 +394,9 @@ def measure_step(cfg_name: str, steps: int, warmup: int, hwm=False, keys="bf16",
         launch_step(t)
     torch.cuda.synchronize()
 
-    # graphs: all R steps (one per input copy), and the first r of them for
-    # the remainder of `steps`; one-step graphs for the replay overhead
+    # graphs: S steps over the R input copies in turn, and the first
+    # steps % S of them for the remainder of `steps`; one-step graphs for the
+    # replay overhead
     cap = torch.cuda.Stream()
     cap.wait_stream(torch.cuda.current_stream())
 
@@ -399,18 +407,19 @@ def measure_step(cfg_name: str, steps: int, warmup: int, hwm=False, keys="bf16",
                 launch_step(t)
         return g
 
-    g_all = capture(sets)
-    rem = steps % R
-    g_rem = capture(sets[:rem]) if rem else None
+    S = R * -(-GRAPH_STEPS // R)
+    g_all = capture([sets[i % R] for i in range(S)])
+    rem = steps % S
+    g_rem = capture([sets[i % R] for i in range(rem)]) if rem else None
     g_one = [capture([t]) for t in sets]
     torch.cuda.synchronize()
 
-    for _ in range(-(-warmup // R)):
+    for _ in range(-(-warmup // S)):
         g_all.replay()
     torch.cuda.synchronize()
     # exactly `steps` steps between one synchronized start and end, with
     # events at the batch boundaries only
-    n_rep = steps // R
+    n_rep = steps // S
     cuts = [round(n_rep * j / BATCHES) for j in range(BATCHES + 1)]
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(BATCHES + 1)]
     evs[0].record()
@@ -424,7 +433,7 @@ def measure_step(cfg_name: str, steps: int, warmup: int, hwm=False, keys="bf16",
         evs[j + 1].record()
     torch.cuda.synchronize()
     total_ms = evs[0].elapsed_time(evs[-1])
-    batch_ms = [evs[j].elapsed_time(evs[j + 1]) / ((cuts[j + 1] - cuts[j]) * R) for j in range(BATCHES - 1)
+    batch_ms = [evs[j].elapsed_time(evs[j + 1]) / ((cuts[j + 1] - cuts[j]) * S) for j in range(BATCHES - 1)
                 if cuts[j + 1] > cuts[j]]
     if not batch_ms:
         batch_ms = [total_ms / steps]
@@ -446,7 +455,7 @@ def measure_step(cfg_name: str, steps: int, warmup: int, hwm=False, keys="bf16",
     valid = int(np.clip(inp.seq_lens if mt is None else mt.seq_lens, 0, N).sum())
     alg = algorithmic_bytes(inp, hwm, T, None if mt is None else mt.seq_lens)
     res = {
-        "inp": inp, "cfg": cfg, "R": R, "valid": valid, "T": T, "alg": alg,
+        "inp": inp, "cfg": cfg, "R": R, "S": S, "valid": valid, "T": T, "alg": alg,
         "ms_per_step": total_ms / steps, "step_us_median_of_batches": _median(batch_ms) * 1e3,
         "one_step_graph_us": one_ms * 1e3,
         "score_us": score_avg_ms * 1e3, "topk_us": topk_avg_ms * 1e3,
@@ -471,7 +480,7 @@ def summary(r: dict) -> dict:
         "score_us": round(r["score_us"], 2), "topk_us": round(r["topk_us"], 2),
         "score_key_GBs": round(r["k_GBs"], 1), "score_key_frac": round(r["k_GBs"] / HBM_PEAK_GBS, 4),
         "score_all_bytes_frac": round(r["all_GBs"] / HBM_PEAK_GBS, 4),
-        "input_copies": r["R"],
+        "input_copies": r["R"], "steps_per_graph": r["S"],
     }
 
 
@@ -560,8 +569,9 @@ def main():
             "max_pages": inp.max_pages, "max_c4": inp.max_c4, "valid_positions": head["valid"],
             "valid_pages": int(wl.pages_needed(inp.seq_lens).sum()), "topk": inp.topk, "seed": cfg.seed,
             "tail": "incremental (row_hwm)" if args.hwm else "stateless full -inf",
-            "input_copies": head["R"],
-            "timing": f"hipGraph replays of {head['R']} consecutive steps [score; top-k], one per input copy; "
+            "input_copies": head["R"], "steps_per_graph": head["S"],
+            "timing": f"hipGraph replays of {head['S']} consecutive steps [score; top-k], the {head['R']} input "
+                      f"copies in turn; "
                       f"HIP events, {BATCHES} batches; one_step_graph_us: graphs of one step each, whose replay "
                       f"adds a fixed launch cost per step",
             "accumulate": "fp32",
@@ -708,17 +718,18 @@ def bench_attention(args, cfg, inp):
                 launch(t)
         return g
 
-    g_all = capture(sets)
-    rem = args.steps % R
-    g_rem = capture(sets[:rem]) if rem else None
+    S = R * -(-GRAPH_STEPS // R)
+    g_all = capture([sets[i % R] for i in range(S)])
+    rem = args.steps % S
+    g_rem = capture([sets[i % R] for i in range(rem)]) if rem else None
     g_one = [capture([t]) for t in sets]
     torch.cuda.synchronize()
-    for _ in range(-(-args.warmup // R)):
+    for _ in range(-(-args.warmup // S)):
         g_all.replay()
     torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record()
-    for _ in range(args.steps // R):
+    for _ in range(args.steps // S):
         g_all.replay()
     if g_rem is not None:
         g_rem.replay()
@@ -755,9 +766,9 @@ def bench_attention(args, cfg, inp):
             "selected_positions": n_sel, "splits": int(nsplit), "scale": att.scale, "seed": cfg.seed,
             "selection": "uniform random subset of min(k, L) positions per request, ascending, -1 padded; "
                          "R such subsets, one per call in turn",
-            "input_copies": R,
-            "timing": f"hipGraph replays of {R} consecutive calls, one per selection (each its own random subset "
-                      f"of the same pages); HIP events; launch_avg_us: median of {BATCHES} batches of 200 "
+            "input_copies": R, "steps_per_graph": S,
+            "timing": f"hipGraph replays of {S} consecutive calls, the {R} selections in turn (each its own random "
+                      f"subset of the same pages); HIP events; launch_avg_us: median of {BATCHES} batches of 200 "
                       f"back-to-back calls; one_step_graph_us: graphs of one call each",
             "accumulate": "fp32 (softmax weights bf16 into the value product)",
         },
